@@ -1,0 +1,136 @@
+"""libkda for PyTorch-ROCm: Kimi Delta Attention chunked forward/backward on MI355X.
+
+The Python layer only marshals arguments: it checks tensor devices, dtypes and
+shapes, allocates outputs with torch (device memory), and passes raw pointers
+plus the current HIP stream to the C ABI of libkda.so.  Every step of the
+computation (normalisation, gating, intra-chunk solve, inter-chunk state
+passing, gradients) runs in the library's HIP kernels.  There is no CPU or
+PyTorch fallback.
+
+Layouts follow include/kda.h: q, k, g ``[T, H, dk]``; v ``[T, H, dv]``;
+beta ``[T, H]`` (the logit); states ``[N, H, dk, dv]`` fp32; cu_seqlens int32
+``[N + 1]`` on the device.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import (KDA_BF16, KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KdaConfig, KdaError, kda_bwd_workspace_size,
+                   kda_fwd_workspace_size, kda_saved_size, make_config)
+
+__all__ = ["kda_fwd", "kda_bwd", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
+           "make_config", "KdaConfig", "KdaError", "KDA_F32", "KDA_BF16", "KDA_FLAG_SAVE_FOR_BWD"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt_code(dtype):
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    if dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _ptr(t):
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _common(q, k, v, g, beta, cu_seqlens, num_seqs):
+    torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [T,H,dk] and v [T,H,dv]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("libkda runs on the GPU only: tensors must be on a cuda (HIP) device")
+    dt = q.dtype
+    for name, t, shp in (("k", k, (T, H, dk)), ("v", v, (T, H, dv)), ("g", g, (T, H, dk)), ("beta", beta, (T, H))):
+        _check(t, name, shp, dt, dev)
+    _check(q, "q", (T, H, dk), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the same device")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    return T, H, dk, dv, N, dev, dt
+
+
+def kda_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: Optional[int] = None,
+            out_dtype=None, save_for_bwd: bool = False, eps: float = 1e-6, scale: float = 1.0,
+            output_final_state: bool = True):
+    """KDA forward.  Returns ``(o, final_state, saved)``; ``saved`` is None
+    unless ``save_for_bwd``.  ``num_seqs`` splits an un-packed stream into equal
+    sequences when ``cu_seqlens`` is None."""
+    torch = _torch()
+    T, H, dk, dv, N, dev, dt = _common(q, k, v, g, beta, cu_seqlens, num_seqs)
+    out_dtype = out_dtype or torch.float32
+    _check(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    cfg = make_config(H, dk, dv, _dt_code(dt), _dt_code(out_dtype), eps, scale,
+                      KDA_FLAG_SAVE_FOR_BWD if save_for_bwd else 0)
+    o = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    saved = None
+    if save_for_bwd:
+        saved = torch.empty(max(kda_saved_size(cfg, T, N), 1), dtype=torch.uint8, device=dev)
+    wsb = kda_fwd_workspace_size(cfg, T, N)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.check(_lib.kda_fwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                    _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(saved), _ptr(ws), wsb, stream))
+    return o, sf, saved
+
+
+def kda_bwd(q, k, v, g, beta, saved, dO, cu_seqlens=None, initial_state=None, dS_final=None, *,
+            num_seqs: Optional[int] = None, out_dtype=None, eps: float = 1e-6, scale: float = 1.0,
+            output_d_initial_state: bool = True):
+    """KDA backward for the loss <dO, o> + <dS_final, final_state>.  Returns a
+    dict with dq, dk, dv, dg, dbeta and dS0 (None unless requested)."""
+    torch = _torch()
+    T, H, dk, dv, N, dev, dt = _common(q, k, v, g, beta, cu_seqlens, num_seqs)
+    out_dtype = out_dtype or torch.float32
+    _check(dO, "dO", (T, H, dv), dt, dev)
+    _check(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    _check(dS_final, "dS_final", (N, H, dk, dv), torch.float32, dev)
+    cfg = make_config(H, dk, dv, _dt_code(dt), _dt_code(out_dtype), eps, scale, 0)
+    need = kda_saved_size(cfg, T, N)
+    if saved is None or saved.dtype != torch.uint8 or saved.numel() < need or saved.device != dev:
+        raise ValueError(f"saved must be a uint8 device tensor of at least {need} bytes from kda_fwd(save_for_bwd=True)")
+    out = {
+        "dq": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+        "dk": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+        "dv": torch.empty((T, H, dv), dtype=out_dtype, device=dev),
+        "dg": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+        "dbeta": torch.empty((T, H), dtype=out_dtype, device=dev),
+        "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_d_initial_state else None,
+    }
+    wsb = kda_bwd_workspace_size(cfg, T, N)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.check(_lib.kda_bwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                    _ptr(initial_state), _ptr(saved), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
+                                    _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                    _ptr(out["dS0"]), _ptr(ws), wsb, stream))
+    return out

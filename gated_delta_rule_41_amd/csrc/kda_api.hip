@@ -1,0 +1,234 @@
+// kda_api.hip -- the C ABI declared in include/kda.h.
+//
+// Validates every argument on the host before any HIP call, sizes the saved
+// and workspace buffers, and hands the work to the kernel launchers.  The
+// library allocates nothing and keeps no global state apart from the
+// thread-local error text.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+kda_status fail(kda_status s, const char* fmt, const char* what = "") {
+    snprintf(g_err, sizeof g_err, fmt, what);
+    return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+size_t state_elem_bytes(const kda_config* c) { return c->in_dtype == KDA_BF16 ? 2 : 4; }
+
+// Config check shared by every entry point.  Returns KDA_OK or a status with
+// the reason left in g_err.
+kda_status check_config(const kda_config* c) {
+    if (!c) return fail(KDA_ERR_INVALID_ARG, "config is NULL%s");
+    if (c->H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1%s");
+    if ((c->dk != 64 && c->dk != 128) || (c->dv != 64 && c->dv != 128))
+        return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 64 or 128%s");
+    if (c->chunk != kda::kChunk) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64%s");
+    if ((c->in_dtype != KDA_F32 && c->in_dtype != KDA_BF16) ||
+        (c->out_dtype != KDA_F32 && c->out_dtype != KDA_BF16))
+        return fail(KDA_ERR_INVALID_ARG, "unknown dtype%s");
+    if (c->in_dtype == KDA_F32 && c->dk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "fp32 inputs support dk = 64 only%s");
+    if (!(c->l2_eps >= 0.f) || !isfinite(c->l2_eps)) return fail(KDA_ERR_INVALID_ARG, "l2_eps must be finite and >= 0%s");
+    if (!isfinite(c->scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite%s");
+    if (c->flags & ~KDA_FLAG_SAVE_FOR_BWD) return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
+    return KDA_OK;
+}
+
+kda_status check_sizes(const kda_config* c, int64_t T, int32_t N, const int32_t* cu) {
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31)%s");
+    if (N < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1%s");
+    if (!cu && (T % N) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is NULL but total_tokens is not a multiple of num_seqs%s");
+    if ((int64_t)N * c->H * (c->dv / kda::kSlice) >= ((int64_t)1 << 31))
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large%s");
+    return KDA_OK;
+}
+
+kda_status need_ptr(const void* p, const char* name) {
+    if (!p) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return KDA_OK;
+}
+
+kda_status opt_ptr(const void* p, const char* name) {
+    if (p && !aligned16(p)) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return KDA_OK;
+}
+
+struct SavedLayout {
+    size_t states, nq, nk, total;
+};
+
+SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
+    SavedLayout s;
+    const size_t st = (size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c);
+    const size_t nrm = (size_t)T * c->H * sizeof(float);
+    s.states = 0;
+    s.nq = align256(st);
+    s.nk = s.nq + align256(nrm);
+    s.total = s.nk + align256(nrm);
+    return s;
+}
+
+}  // namespace
+
+#define KDA_TRY(x)                       \
+    do {                                 \
+        kda_status _s = (x);             \
+        if (_s != KDA_OK) return _s;     \
+    } while (0)
+
+extern "C" {
+
+void kda_config_init(kda_config* cfg, int32_t H, int32_t dk, int32_t dv) {
+    if (!cfg) return;
+    memset(cfg, 0, sizeof *cfg);
+    cfg->H = H;
+    cfg->dk = dk;
+    cfg->dv = dv;
+    cfg->chunk = kda::kChunk;
+    cfg->in_dtype = KDA_F32;
+    cfg->out_dtype = KDA_F32;
+    cfg->l2_eps = 1e-6f;
+    cfg->scale = 1.0f;
+    cfg->flags = 0;
+}
+
+size_t kda_saved_size(const kda_config* cfg, int64_t T, int32_t N) {
+    if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
+    return saved_layout(cfg, T, N).total;
+}
+
+size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
+    (void)cfg; (void)T; (void)N;
+    return 0;
+}
+
+size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
+    if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
+    // dL/dS at the end of every chunk, same storage type as the saved states
+    return align256((size_t)kda::num_slots(T, N) * cfg->H * cfg->dk * cfg->dv * state_elem_bytes(cfg));
+}
+
+kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
+                   const void* v, const void* g, const void* beta, const int32_t* cu,
+                   const float* s0, void* o, float* sfinal, void* saved, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    KDA_TRY(check_config(cfg));
+    KDA_TRY(check_sizes(cfg, T, N, cu));
+    if (T > 0) {
+        KDA_TRY(need_ptr(q, "q"));
+        KDA_TRY(need_ptr(k, "k"));
+        KDA_TRY(need_ptr(v, "v"));
+        KDA_TRY(need_ptr(g, "g"));
+        KDA_TRY(need_ptr(beta, "beta"));
+        KDA_TRY(need_ptr(o, "o"));
+    }
+    KDA_TRY(opt_ptr(cu, "cu_seqlens"));
+    KDA_TRY(opt_ptr(s0, "initial_state"));
+    KDA_TRY(opt_ptr(sfinal, "final_state"));
+    KDA_TRY(opt_ptr(workspace, "workspace"));
+    const bool save = (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) != 0;
+    if (save) KDA_TRY(need_ptr(saved, "saved"));
+    if (workspace_bytes < kda_fwd_workspace_size(cfg, T, N))
+        return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
+
+    kda::FwdParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.b = beta;
+    p.cu = cu; p.s0 = s0; p.o = o; p.sfinal = sfinal;
+    if (save) {
+        const SavedLayout L = saved_layout(cfg, T, N);
+        char* base = (char*)saved;
+        p.st_saved = base + L.states;
+        p.nq_saved = (float*)(base + L.nq);
+        p.nk_saved = (float*)(base + L.nk);
+    }
+    p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
+    p.seqlen = cu ? 0 : (int32_t)(T / N);
+    p.eps = cfg->l2_eps; p.scale = cfg->scale;
+    p.nslices = cfg->dv / kda::kSlice;
+    hipError_t e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+kda_status kda_bwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
+                   const void* v, const void* g, const void* beta, const int32_t* cu,
+                   const float* s0, const void* saved, const void* dO, const float* dSf, void* dq,
+                   void* dk, void* dv, void* dg, void* dbeta, float* dS0, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    KDA_TRY(check_config(cfg));
+    KDA_TRY(check_sizes(cfg, T, N, cu));
+    if (T > 0) {
+        KDA_TRY(need_ptr(q, "q"));
+        KDA_TRY(need_ptr(k, "k"));
+        KDA_TRY(need_ptr(v, "v"));
+        KDA_TRY(need_ptr(g, "g"));
+        KDA_TRY(need_ptr(beta, "beta"));
+        KDA_TRY(need_ptr(dO, "dO"));
+        KDA_TRY(need_ptr(dq, "dq"));
+        KDA_TRY(need_ptr(dk, "dk"));
+        KDA_TRY(need_ptr(dv, "dv"));
+        KDA_TRY(need_ptr(dg, "dg"));
+        KDA_TRY(need_ptr(dbeta, "dbeta"));
+    }
+    KDA_TRY(need_ptr(saved, "saved"));
+    KDA_TRY(opt_ptr(cu, "cu_seqlens"));
+    KDA_TRY(opt_ptr(s0, "initial_state"));
+    KDA_TRY(opt_ptr(dSf, "dS_final"));
+    KDA_TRY(opt_ptr(dS0, "d_initial_state"));
+    const size_t need = kda_bwd_workspace_size(cfg, T, N);
+    if (need > 0) KDA_TRY(need_ptr(workspace, "workspace"));
+    if (workspace_bytes < need) return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
+
+    kda::BwdParams p;
+    memset(&p, 0, sizeof p);
+    const SavedLayout L = saved_layout(cfg, T, N);
+    const char* base = (const char*)saved;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.b = beta; p.cu = cu;
+    p.st_saved = base + L.states;
+    p.nq_saved = (const float*)(base + L.nq);
+    p.nk_saved = (const float*)(base + L.nk);
+    p.dO = dO; p.dS_final = dSf;
+    p.dst_saved = workspace;
+    p.dq = dq; p.dk = dk; p.dv_out = dv; p.dg = dg; p.db = dbeta; p.dS0 = dS0;
+    p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
+    p.seqlen = cu ? 0 : (int32_t)(T / N);
+    p.eps = cfg->l2_eps; p.scale = cfg->scale;
+    p.nslices = cfg->dv / kda::kSlice;
+    (void)s0;
+    hipError_t e = kda::launch_bwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_WORKSPACE: return "workspace or saved buffer too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_err; }
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// kda_device.h -- device helpers shared by the libkda kernels (gfx950 only).
+//
+// MFMA wrappers, operand fragments and the LDS position permutation used by
+// the chunked KDA kernels.  Everything here is written for CDNA4 wave64:
+//
+//  * v_mfma_f32_16x16x32_bf16 ("k32"): lane l supplies A[m = l%16][k = 8(l/16)+j]
+//    and B[k = 8(l/16)+j][n = l%16] for j = 0..7; it receives
+//    D[4(l/16)+i][l%16] for i = 0..3 (the accumulator layout).
+//  * v_mfma_f32_16x16x16_bf16 ("k16"): A[m][4(l/16)+j], B[4(l/16)+j][n], j=0..3.
+//    Its B layout equals the accumulator layout, so a 16x16 accumulator block
+//    can be fed back as the B operand of a k16 product without moving data.
+//  * fp32 operands use v_mfma_f32_16x16x4_f32: a k32 (k16) step becomes 8 (4)
+//    k4 steps, step j taking the j-th element of every lane's fragment.  Any
+//    assignment of logical k to (lane group, element) is valid as long as A and
+//    B use the same one.
+//
+// "Accumulator-compatible" k32 fragments: two stacked accumulator blocks (rows
+// 0..15 and 16..31 of the contraction index) give lane group qg the logical k
+// {4qg..4qg+3, 16+4qg..16+4qg+3}.  Tiles that meet such a B operand are stored
+// in LDS with their contraction index permuted inside every 32-block by perm32
+// below, so the matching A fragment is again 8 contiguous elements.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct V8;
+template <> struct V8<bf16> { typedef bf16x8 t; };
+template <> struct V8<float> { typedef f32x8 t; };
+template <typename T> struct V4;
+template <> struct V4<bf16> { typedef bf16x4 t; };
+template <> struct V4<float> { typedef f32x4 t; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x4 mma_k32(f32x4 c, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k32(f32x4 c, f32x8 a, f32x8 b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4 mma_k16(f32x4 c, bf16x4 a, bf16x4 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(f32x4 c, f32x4 a, f32x4 b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+
+// ------------------------------------------------------------ fragments
+template <typename T> __device__ __forceinline__ typename V8<T>::t pack8(f32x4 lo, f32x4 hi);
+template <> __device__ __forceinline__ bf16x8 pack8<bf16>(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { r[j] = (bf16)lo[j]; r[j + 4] = (bf16)hi[j]; }
+    return r;
+}
+template <> __device__ __forceinline__ f32x8 pack8<float>(f32x4 lo, f32x4 hi) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { r[j] = lo[j]; r[j + 4] = hi[j]; }
+    return r;
+}
+template <typename T> __device__ __forceinline__ typename V4<T>::t pack4(f32x4 x);
+template <> __device__ __forceinline__ bf16x4 pack4<bf16>(f32x4 x) {
+    bf16x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
+    return r;
+}
+template <> __device__ __forceinline__ f32x4 pack4<float>(f32x4 x) { return x; }
+
+
+__device__ __forceinline__ f32x4 unpack4(bf16x4 x) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (float)x[j];
+    return r;
+}
+__device__ __forceinline__ f32x4 unpack4(f32x4 x) { return x; }
+
+// hi = T(x); lo = T(x - hi) when SPLIT (the pair carries ~16 mantissa bits).
+template <typename T, bool SPLIT>
+__device__ __forceinline__ void sts4_split(T* hi, T* lo, f32x4 x) {
+    const typename V4<T>::t h = pack4<T>(x);
+    *reinterpret_cast<typename V4<T>::t*>(hi) = h;
+    if constexpr (SPLIT) *reinterpret_cast<typename V4<T>::t*>(lo) = pack4<T>(x - unpack4(h));
+}
+template <typename T, bool SPLIT>
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, typename V8<T>::t& hi, typename V8<T>::t& lo) {
+    hi = pack8<T>(a, b);
+    if constexpr (SPLIT) {
+        f32x4 ra, rb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { ra[j] = a[j] - to_f32(hi[j]); rb[j] = b[j] - to_f32(hi[j + 4]); }
+        lo = pack8<T>(ra, rb);
+    } else {
+        lo = hi;
+    }
+}
+
+__device__ __forceinline__ bf16x4 neg4(bf16x4 x) {
+    return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u16x4, x) ^ (unsigned short)0x8000);
+}
+__device__ __forceinline__ f32x4 neg4(f32x4 x) { return -x; }
+
+// 8 contiguous elements from LDS (16-byte aligned for bf16, 32-byte for fp32).
+template <typename T> __device__ __forceinline__ typename V8<T>::t lds8(const T* p) {
+    return *reinterpret_cast<const typename V8<T>::t*>(p);
+}
+template <typename T> __device__ __forceinline__ typename V4<T>::t lds4(const T* p) {
+    return *reinterpret_cast<const typename V4<T>::t*>(p);
+}
+template <typename T> __device__ __forceinline__ void sts4(T* p, f32x4 x) {
+    *reinterpret_cast<typename V4<T>::t*>(p) = pack4<T>(x);
+}
+// 4 contiguous elements of type T from LDS, widened to fp32.
+template <typename T> __device__ __forceinline__ f32x4 lds4f(const T* p) {
+    typename V4<T>::t v = lds4<T>(p);
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = to_f32(v[j]);
+    return r;
+}
+
+// Position of contraction index k inside its 32-block for tiles that meet an
+// accumulator-compatible fragment: logical {16h + 4qg + j} -> 8qg + 4h + j.
+__device__ __forceinline__ int perm32(int k) {
+    const int kk = k & 31;
+    return (k & ~31) | (((kk >> 2) & 3) << 3) | ((kk >> 4) << 2) | (kk & 3);
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// ---------------------------------------------------- global loads/stores
+// Loads N consecutive elements of type T (N*sizeof(T) in {8,16,32} bytes)
+// and widens them to fp32.
+template <typename T, int N> struct GVec {
+    float v[N];
+};
+template <typename T, int N>
+__device__ __forceinline__ void gload(float (&dst)[N], const T* __restrict__ src) {
+    if constexpr (sizeof(T) == 2) {
+        static_assert(N == 4 || N == 8, "bf16 row piece");
+        if constexpr (N == 8) {
+            u16x8 raw = *reinterpret_cast<const u16x8*>(src);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = __uint_as_float(((unsigned)raw[j]) << 16);
+        } else {
+            u16x4 raw = *reinterpret_cast<const u16x4*>(src);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[j] = __uint_as_float(((unsigned)raw[j]) << 16);
+        }
+    } else {
+        static_assert(N % 4 == 0, "fp32 row piece");
+#pragma unroll
+        for (int j = 0; j < N; j += 4) {
+            f32x4 x = *reinterpret_cast<const f32x4*>(src + j);
+            dst[j] = x[0]; dst[j + 1] = x[1]; dst[j + 2] = x[2]; dst[j + 3] = x[3];
+        }
+    }
+}
+
+template <typename T> __device__ __forceinline__ float gload1(const T* p) { return to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void gstore1(T* p, float x) { *p = from_f32<T>(x); }
+
+}  // namespace kda

@@ -1,0 +1,67 @@
+// kda_internal.h -- host-side interface between the C ABI (kda_api.hip) and
+// the kernel launchers.  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;      // tokens per chunk
+constexpr int kSlice = 64;      // value columns per forward / reverse-scan workgroup
+constexpr int kThreads = 256;   // 4 wave64 per workgroup
+
+// Per-chunk state slots: chunk j of sequence n uses slot floor(cu[n]/64) + n + j.
+// The map is collision-free and bounded by floor(T/64) + N (see kda_api.hip).
+inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* b;
+    const int32_t* cu;   // device [N+1] or nullptr (equal sequences of `seqlen`)
+    const float* s0;     // [N,H,dk,dv] or nullptr
+    void* o;             // [T,H,dv] out dtype
+    float* sfinal;       // [N,H,dk,dv] or nullptr
+    void* st_saved;      // [slots,H,dk,dv] state dtype, or nullptr
+    float* nq_saved;     // [T,H] or nullptr
+    float* nk_saved;     // [T,H] or nullptr
+    int64_t T;
+    int32_t N, H, dv, seqlen;
+    float eps, scale;
+    int32_t nslices;     // dv / kSlice
+};
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* b;
+    const int32_t* cu;
+    const void* st_saved;    // forward-entering state of every chunk
+    const float* nq_saved;
+    const float* nk_saved;
+    const void* dO;          // [T,H,dv] in dtype
+    const float* dS_final;   // [N,H,dk,dv] or nullptr
+    void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
+    void* dq;
+    void* dk;
+    void* dv_out;
+    void* dg;
+    void* db;
+    float* dS0;              // [N,H,dk,dv] or nullptr
+    int64_t T;
+    int32_t N, H, dv, seqlen;
+    float eps, scale;
+    int32_t nslices;
+};
+
+// in_dtype / out_dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save,
+                      hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, hipStream_t stream);
+
+}  // namespace kda

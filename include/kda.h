@@ -1,0 +1,140 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) chunked forward and
+ * backward on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The pages describe KDA in words: per head, a gated
+ * matrix-valued state is read and written token by token in place of attention
+ * over all past keys and values ("TorchTitan Ascend open source: Kimi K3.1 Pro
+ * adaptation and training practice", jinguxun.com news 11080097, section
+ * "Kimi K3.1 Pro model structure").  libkda implements the gated delta rule as
+ * that recurrence.  For each document and head, with S a dk x dv fp32 state:
+ *
+ *     qh_t = scale * q_t / sqrt(|q_t|^2 + eps),  kh_t = k_t / sqrt(|k_t|^2 + eps)
+ *     beta_t = sigmoid(b_t),   alpha_t = exp(g_t)          (g_t <= 0, per key channel)
+ *     S_t  = (I - beta_t kh_t kh_t^T) Diag(alpha_t) S_{t-1} + beta_t kh_t v_t^T
+ *     o_t  = S_t^T qh_t
+ *
+ * The work is organised as intra-chunk processing plus inter-chunk state
+ * passing, with the Q/K normalisation, the beta transform and the gating fused
+ * into the forward, and the backward reusing the statistics and states the
+ * forward saved (same page, section "KDA pre/post-processing fusion"; also
+ * "Ascend implements LoRA training of Kimi K3.1 Pro", jinguxun.com news
+ * 11045563, section "KDA: big fused forward and backward").  Packed sequences
+ * with document boundaries are supported through cu_seqlens (page 11080097,
+ * section "Kimi K3.1 Pro Ascend training adaptation").  The chunking changes
+ * only rounding, never the result.
+ *
+ * Conventions for every entry point.
+ *  - Layouts (row-major, contiguous, token-major packed):
+ *      q, k, g : [total_tokens, H, dk]      v, o, dO : [total_tokens, H, dv]
+ *      beta    : [total_tokens, H]          (the logit b; sigmoid is applied inside)
+ *      states  : [num_seqs, H, dk, dv] fp32 (dk is the outer index)
+ *      cu_seqlens : [num_seqs + 1] int32 in device memory; cu[0] = 0,
+ *                   non-decreasing, cu[num_seqs] = total_tokens.  NULL means
+ *                   num_seqs equal sequences of total_tokens / num_seqs tokens.
+ *  - All pointers except the config are device pointers (hipMalloc'ed or
+ *    equivalent), 16-byte aligned, and owned by the caller.  Inputs are read
+ *    only; outputs are fully overwritten.  The library never allocates, frees,
+ *    synchronises or changes the current device, and keeps no global state:
+ *    every entry point is re-entrant.  All work is enqueued on `stream` (a
+ *    hipStream_t passed as void*; NULL is the null stream).
+ *  - Errors.  Arguments are validated on the host BEFORE any HIP call; a bad
+ *    argument returns KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED /
+ *    KDA_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *    KDA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  kda_last_error() returns a thread-local description of
+ *    the last failure.  No exception crosses this boundary.
+ *  - cu_seqlens contents live on the device and are not checked on the host.
+ *    A malformed cu_seqlens (decreasing, or last entry != total_tokens) is
+ *    undefined behaviour; the kernels clamp every document to
+ *    [0, total_tokens) so it cannot address memory outside the buffers.
+ *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
+ *    {KDA_F32, KDA_BF16}; H >= 1; total_tokens < 2^31; per-chunk cumulative
+ *    log-decay sum_{chunk} g >= -80 per channel (the kernels factor
+ *    exp(G_r - G_s) = exp(G_r) exp(-G_s) inside a 64-token chunk).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer   */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dk, dv, chunk...) */
+    KDA_ERR_WORKSPACE = 3,   /* workspace or saved buffer too small          */
+    KDA_ERR_HIP = 4          /* a HIP runtime call or launch failed          */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* kda_config.flags */
+#define KDA_FLAG_SAVE_FOR_BWD 1u /* forward also fills `saved` for kda_bwd */
+
+typedef struct kda_config {
+    int32_t H;         /* heads                                        */
+    int32_t dk;        /* key / query head dim (64 or 128)             */
+    int32_t dv;        /* value head dim (64 or 128)                   */
+    int32_t chunk;     /* chunk length; must be 64                     */
+    int32_t in_dtype;  /* kda_dtype of q, k, v, g, beta, dO            */
+    int32_t out_dtype; /* kda_dtype of o, dq, dk, dv, dg, dbeta        */
+    float l2_eps;      /* eps inside the L2 norm (1e-6 by default)     */
+    float scale;       /* multiplies the normalised query (1.0)        */
+    uint32_t flags;    /* KDA_FLAG_*                                   */
+} kda_config;
+
+/* Fill *cfg with defaults: chunk 64, eps 1e-6, scale 1, fp32/fp32, no flags. */
+void kda_config_init(kda_config* cfg, int32_t H, int32_t dk, int32_t dv);
+
+/* Sizes in bytes (pure host functions; 0 for an invalid config).
+ * kda_saved_size: the buffer kda_fwd fills under KDA_FLAG_SAVE_FOR_BWD and
+ * kda_bwd reads: per-chunk entering states plus the per-token q/k norms.
+ * kda_fwd_workspace_size / kda_bwd_workspace_size: scratch for one call. */
+size_t kda_saved_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
+size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
+size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
+
+/* Forward.  o: [total_tokens, H, dv] in out_dtype.  initial_state: fp32
+ * [num_seqs, H, dk, dv] or NULL (zero state; every document starts from its
+ * own entry, never from the previous document).  final_state: fp32
+ * [num_seqs, H, dk, dv] or NULL.  saved: required (kda_saved_size bytes) iff
+ * flags has KDA_FLAG_SAVE_FOR_BWD, else ignored.  workspace may be NULL when
+ * kda_fwd_workspace_size() is 0. */
+kda_status kda_fwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
+                   const void* k, const void* v, const void* g, const void* beta,
+                   const int32_t* cu_seqlens, const float* initial_state, void* o,
+                   float* final_state, void* saved, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Backward of kda_fwd for the loss <dO, o> + <dS_final, final_state>.
+ * Takes the same inputs as the forward plus `saved` (filled by a forward with
+ * KDA_FLAG_SAVE_FOR_BWD on the same inputs), dO ([total_tokens, H, dv],
+ * in_dtype) and dS_final (fp32 [num_seqs, H, dk, dv] or NULL = 0).
+ * Outputs, all in out_dtype: dq, dk, dg [total_tokens, H, dk] (gradients with
+ * respect to the RAW q and k, through the L2 norm, and to g, the log-decay);
+ * dv [total_tokens, H, dv]; dbeta [total_tokens, H] (with respect to the
+ * logit b).  d_initial_state: fp32 [num_seqs, H, dk, dv] or NULL.
+ * workspace: kda_bwd_workspace_size() bytes. */
+kda_status kda_bwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
+                   const void* k, const void* v, const void* g, const void* beta,
+                   const int32_t* cu_seqlens, const float* initial_state, const void* saved,
+                   const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                   void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status s);
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* kda_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -74,11 +74,15 @@ def _load():
     return lib
 
 
+MAX_THREADS = 16  # the CPU share a one-GPU machine grants, whatever the host reports
+
+
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
 
 
 def _f64(x):

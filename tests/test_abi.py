@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, sizes buffers as documented, and rejects bad arguments
+on the host with the documented status BEFORE any HIP call (every case below
+fails validation, so no pointer is ever dereferenced and nothing is launched)."""
+import ctypes
+
+import pytest
+
+from gated_delta_rule_41_amd import _lib
+from gated_delta_rule_41_amd._lib import (KDA_BF16, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE,
+                                          KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KDA_OK)
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def test_library_exports_every_header_function():
+    lib = _lib.load()
+    names = _lib.header_functions()
+    assert {"kda_fwd", "kda_bwd", "kda_saved_size", "kda_config_init"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.kda_version() >= 100
+
+
+def test_config_init_defaults():
+    cfg = _lib.make_config(4, 128, 64)
+    assert (cfg.H, cfg.dk, cfg.dv, cfg.chunk) == (4, 128, 64, 64)
+    assert abs(cfg.l2_eps - 1e-6) < 1e-12 and cfg.scale == 1.0
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(5):
+        assert lib.kda_status_string(s)
+    assert b"unknown" in lib.kda_status_string(99)
+
+
+def test_sizes():
+    cfg = _lib.make_config(32, 128, 128, KDA_BF16, KDA_F32)
+    T, N = 4 * 8192, 4
+    slots = T // 64 + N
+    states = slots * 32 * 128 * 128 * 2
+    nrm = T * 32 * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm)
+    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states)
+    assert _lib.kda_fwd_workspace_size(cfg, T, N) == 0
+    cfg32 = _lib.make_config(2, 64, 64, KDA_F32, KDA_F32)
+    assert _lib.kda_saved_size(cfg32, 256, 1) == al(5 * 2 * 64 * 64 * 4) + 2 * al(256 * 2 * 4)
+    bad = _lib.make_config(2, 96, 64)
+    assert _lib.kda_saved_size(bad, 256, 1) == 0
+
+
+def _fwd(cfg, T=128, N=1, q=FAKE, o=FAKE, cu=0, saved=0, ws=0, wsb=0):
+    return _lib.kda_fwd_raw(cfg, T, N, q, FAKE, FAKE, FAKE, FAKE, cu, 0, o, 0, saved, ws, wsb, 0)
+
+
+def _err():
+    return _lib.load().kda_last_error().decode()
+
+
+@pytest.mark.parametrize("dk,dv,chunk,ind,expect", [
+    (96, 128, 64, KDA_BF16, KDA_ERR_UNSUPPORTED),
+    (128, 32, 64, KDA_BF16, KDA_ERR_UNSUPPORTED),
+    (128, 128, 32, KDA_BF16, KDA_ERR_UNSUPPORTED),
+    (128, 128, 64, KDA_F32, KDA_ERR_UNSUPPORTED),
+    (128, 128, 64, 7, KDA_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_unsupported_configs(dk, dv, chunk, ind, expect):
+    cfg = _lib.make_config(2, 64, 64)
+    cfg.dk, cfg.dv, cfg.chunk, cfg.in_dtype = dk, dv, chunk, ind
+    assert _fwd(cfg) == expect
+    assert _err()
+
+
+def test_fwd_rejects_bad_arguments():
+    cfg = _lib.make_config(2, 64, 64, KDA_BF16)
+    assert _lib.load().kda_fwd(None, 1, 1, *([None] * 11), 0, None) == KDA_ERR_INVALID_ARG
+    assert _fwd(cfg, T=-1) == KDA_ERR_INVALID_ARG
+    assert _fwd(cfg, T=1 << 31) == KDA_ERR_INVALID_ARG
+    assert _fwd(cfg, N=0) == KDA_ERR_INVALID_ARG
+    assert _fwd(cfg, T=100, N=3) == KDA_ERR_INVALID_ARG      # no cu_seqlens and T % N != 0
+    assert _fwd(cfg, q=0) == KDA_ERR_INVALID_ARG and "q" in _err()
+    assert _fwd(cfg, o=0) == KDA_ERR_INVALID_ARG and "o" in _err()
+    assert _fwd(cfg, q=FAKE + 2) == KDA_ERR_INVALID_ARG and "aligned" in _err()
+    assert _fwd(cfg, cu=FAKE + 4) == KDA_ERR_INVALID_ARG
+    cfg.flags = KDA_FLAG_SAVE_FOR_BWD
+    assert _fwd(cfg) == KDA_ERR_INVALID_ARG and "saved" in _err()
+    cfg.flags = 1 << 5
+    assert _fwd(cfg) == KDA_ERR_INVALID_ARG
+    cfg.flags = 0
+    cfg.l2_eps = float("nan")
+    assert _fwd(cfg) == KDA_ERR_INVALID_ARG
+    cfg.l2_eps = 1e-6
+    cfg.scale = float("inf")
+    assert _fwd(cfg) == KDA_ERR_INVALID_ARG
+
+
+def test_bwd_rejects_bad_arguments():
+    cfg = _lib.make_config(2, 64, 64, KDA_BF16)
+    T, N = 128, 1
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=0, s0=0, saved=FAKE, dO=FAKE, dSf=0, dq=FAKE,
+                dk=FAKE, dv=FAKE, dg=FAKE, db=FAKE, dS0=0, ws=FAKE)
+    need = _lib.kda_bwd_workspace_size(cfg, T, N)
+    assert need > 0
+
+    def call(wsb=need, **kw):
+        a = dict(args)
+        a.update(kw)
+        return _lib.kda_bwd_raw(cfg, T, N, a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["s0"], a["saved"],
+                                a["dO"], a["dSf"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dS0"], a["ws"], wsb, 0)
+
+    assert call(wsb=need - 1) == KDA_ERR_WORKSPACE
+    assert call(saved=0) == KDA_ERR_INVALID_ARG and "saved" in _err()
+    assert call(dO=0) == KDA_ERR_INVALID_ARG and "dO" in _err()
+    assert call(dg=FAKE + 8) == KDA_ERR_INVALID_ARG
+    assert call(ws=0) == KDA_ERR_INVALID_ARG
+    cfg.dk = 80
+    assert call() == KDA_ERR_UNSUPPORTED
+
+
+def test_python_layer_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import gated_delta_rule_41_amd as kda
+    x = torch.zeros(4, 1, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_fwd(x, x, x, x, torch.zeros(4, 1))
+    assert KDA_OK == 0
+    assert isinstance(_lib.KdaConfig(), ctypes.Structure)
