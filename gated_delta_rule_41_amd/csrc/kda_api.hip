@@ -24,7 +24,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-size_t state_elem_bytes(const kda_config* c) { return c->in_dtype == KDA_BF16 ? 2 : 4; }
+// Saved per-chunk states and state gradients are fp32 for every input dtype.
+size_t state_elem_bytes(const kda_config* c) { (void)c; return 4; }
 
 // Config check shared by every entry point.  Returns KDA_OK or a status with
 // the reason left in g_err.

@@ -184,4 +184,45 @@ template <typename T> __device__ __forceinline__ float gload1(const T* p) { retu
 
 template <typename T> __device__ __forceinline__ void gstore1(T* p, float x) { *p = from_f32<T>(x); }
 
+// ------------------------------------------------------- work mapping
+// Block -> (chain, slice).  Slices of one chain get block ids b and b+8, which
+// the dispatcher places on the same XCD, so their duplicate q/k/g reads share
+// that XCD's L2.
+__device__ __forceinline__ void map_block(int b, int nchains, int ns, int& chain, int& slice) {
+    const int total = nchains * ns;
+    if (ns > 1 && (total % (8 * ns)) == 0) {
+        const int x = b & 7, r = b >> 3;
+        slice = r % ns;
+        chain = (r / ns) * 8 + x;
+    } else {
+        chain = b / ns;
+        slice = b % ns;
+    }
+}
+
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int seqlen, int64_t T,
+                                           int64_t& t0, int64_t& t1) {
+    if (cu) {
+        int64_t a = cu[n], z = cu[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        z = z < a ? a : (z > T ? T : z);
+        t0 = a;
+        t1 = z;
+    } else {
+        t0 = (int64_t)n * seqlen;
+        t1 = t0 + seqlen;
+    }
+}
+
+// acc += A.B with optional hi/lo operands: Ah.Bh + Ah.Bl + Al.Bh.
+template <bool SPLIT, typename V>
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, const V& ah, const V& al, const V& bh, const V& bl) {
+    acc = mma_k32(acc, ah, bh);
+    if constexpr (SPLIT) {
+        acc = mma_k32(acc, ah, bl);
+        acc = mma_k32(acc, al, bh);
+    }
+    return acc;
+}
+
 }  // namespace kda

@@ -63,46 +63,6 @@ struct __attribute__((aligned(32))) FwdSmem {
     float red[4][DK];         // per-wave column sums of g
 };
 
-// Block -> (chain, slice).  Slices of one chain get block ids b and b+8, which
-// the dispatcher places on the same XCD, so their duplicate q/k/g reads share
-// that XCD's L2.
-__device__ __forceinline__ void map_block(int b, int nchains, int ns, int& chain, int& slice) {
-    const int total = nchains * ns;
-    if (ns > 1 && (total % (8 * ns)) == 0) {
-        const int x = b & 7, r = b >> 3;
-        slice = r % ns;
-        chain = (r / ns) * 8 + x;
-    } else {
-        chain = b / ns;
-        slice = b % ns;
-    }
-}
-
-__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int seqlen, int64_t T,
-                                           int64_t& t0, int64_t& t1) {
-    if (cu) {
-        int64_t a = cu[n], z = cu[n + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        z = z < a ? a : (z > T ? T : z);
-        t0 = a;
-        t1 = z;
-    } else {
-        t0 = (int64_t)n * seqlen;
-        t1 = t0 + seqlen;
-    }
-}
-
-// acc += A.B with optional hi/lo operands: Ah.Bh + Ah.Bl + Al.Bh.
-template <bool SPLIT, typename V>
-__device__ __forceinline__ f32x4 mma3(f32x4 acc, const V& ah, const V& al, const V& bh, const V& bl) {
-    acc = mma_k32(acc, ah, bh);
-    if constexpr (SPLIT) {
-        acc = mma_k32(acc, ah, bl);
-        acc = mma_k32(acc, al, bh);
-    }
-    return acc;
-}
-
 template <typename T, typename TO, int DK, bool SAVE>
 __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
     __shared__ FwdSmem<T, DK> sm;
@@ -404,11 +364,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) split8<T, SPLIT>(S[2 * kk], S[2 * kk + 1], sfh[kk], sfl[kk]);
         if (SAVE) {
-            T* st = reinterpret_cast<T*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
+            // entering state of this chunk, fp32 (the backward's state-coupled
+            // gradient terms need more than bf16 precision)
+            float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = from_f32<T>(S[mb][i]);
+                for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
         }
         // U = Ut - W S   (the tile holds -W)
 #pragma unroll

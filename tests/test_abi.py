@@ -39,7 +39,7 @@ def test_sizes():
     cfg = _lib.make_config(32, 128, 128, KDA_BF16, KDA_F32)
     T, N = 4 * 8192, 4
     slots = T // 64 + N
-    states = slots * 32 * 128 * 128 * 2
+    states = slots * 32 * 128 * 128 * 4
     nrm = T * 32 * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm)
