@@ -1,0 +1,181 @@
+"""Benchmark: KDA forward + backward on one MI355X.
+
+Workload: B=4 packed sequences x T=8192 tokens, H=32 heads, dk=dv=128, chunk 64,
+bf16 inputs (q, k, v, g, beta logit, dO), fp32 state, fp32 outputs and
+gradients; seeded synthetic inputs from kda_inputs (the same recipe the parity
+tests use).  One step = one training pass of the whole hot path: kda_fwd with
+the state save, then kda_bwd (reverse state scan + chunk-parallel gradients).
+
+Prints ONE JSON line.  `value` is whole-job tokens/s of the fwd+bwd step with
+inputs already resident in HBM.  `roofline` reports the dominant kernel of the
+step against the HBM roofline; `roofline_fwd` reports the fused forward on its
+own (inference call, no state save).  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+
+Algorithmic bytes (inputs read once, outputs written once; anything the
+implementation saves or recomputes is not counted):
+  forward  per token-head: q, k, g (dk bf16 each) + v (dv bf16) + beta (bf16)
+           + o (dv fp32); per (sequence, head): initial + final state (fp32)
+  backward per token-head: q, k, g, v, beta, dO (bf16) + dq, dk, dg, dv, dbeta
+           (fp32); per (sequence, head): initial state, dS_final, d(initial state)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def alg_bytes(B, T, H, dk, dv, mode):
+    th = B * T * H
+    fwd = th * (3 * dk * 2 + dv * 2 + 2 + dv * 4) + B * H * 2 * dk * dv * 4
+    bwd = th * (3 * dk * 2 + dv * 2 + 2 + dv * 2) + th * (3 * dk * 4 + dv * 4 + 4) + B * H * 3 * dk * dv * 4
+    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[mode]
+
+
+def cpu_baseline(x, cu, spec, heads):
+    """fp64 oracle, forward + backward, on the first sequence and `heads` heads."""
+    import numpy as np
+
+    import oracle
+
+    T = spec["T"]
+    sel = {k: np.ascontiguousarray(x[k][:T, :heads]) for k in ("q", "k", "v", "g", "b", "dO")}
+    s0 = np.ascontiguousarray(x["s0"][:1, :heads])
+    dS = np.ascontiguousarray(x["dS"][:1, :heads])
+    threads = min(oracle.default_threads(), heads)
+    t0 = time.perf_counter()
+    oracle.fwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], initial_state=s0, threads=threads)
+    oracle.bwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], sel["dO"], initial_state=s0, dS_final=dS,
+               threads=threads)
+    dt = time.perf_counter() - t0
+    full_tokens = T * heads / spec["H"]   # token-heads processed, as whole tokens of the workload
+    return {"value": full_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd of sequence 0, heads 0..{heads - 1}, T={T} ({T * heads} token-heads), "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's CPU sample (0: skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_41_amd as kda
+    import kda_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda", 0)
+    spec, cu, x = kda_inputs.workload(2)
+    B, T, H, dk, dv = spec["B"], spec["T"], spec["H"], spec["dk"], spec["dv"]
+
+    def to_dev(a):
+        return torch.from_numpy(a).to(dev, torch.bfloat16)
+
+    q, k, v, g, b, dO = (to_dev(x[n]) for n in ("q", "k", "v", "g", "b", "dO"))
+    s0 = torch.from_numpy(x["s0"]).to(dev)
+    dS = torch.from_numpy(x["dS"]).to(dev)
+    cu_t = torch.from_numpy(cu.astype(np.int32)).to(dev)
+
+    def fwd_train():
+        return kda.kda_fwd(q, k, v, g, b, cu_t, s0, save_for_bwd=True)
+
+    def bwd(saved):
+        return kda.kda_bwd(q, k, v, g, b, saved, dO, cu_t, s0, dS)
+
+    for _ in range(args.warmup):
+        _, _, saved = fwd_train()
+        bwd(saved)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        _, _, saved = fwd_train()
+        ev[i][1].record(stream)
+        bwd(saved)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # the inference forward on its own (no state save): the fused forward kernel alone
+    n_inf = max(5, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        kda.kda_fwd(q, k, v, g, b, cu_t, s0)
+    e0.record(stream)
+    for _ in range(n_inf):
+        kda.kda_fwd(q, k, v, g, b, cu_t, s0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    inf_ms = e0.elapsed_time(e1) / n_inf
+
+    tokens = B * T
+    fb_bytes = alg_bytes(B, T, H, dk, dv, "fwdbwd")
+    f_bytes = alg_bytes(B, T, H, dk, dv, "fwd")
+    b_bytes = alg_bytes(B, T, H, dk, dv, "bwd")
+    # dominant kernel launch of the step: the backward call (two kernels) or the forward call
+    if bwd_ms >= fwd_ms:
+        dom = {"kernel": "kda_bwd (state scan + chunk gradients)", "ms": bwd_ms, "bytes": b_bytes}
+    else:
+        dom = {"kernel": "kda_fwd_kernel (training, state save)", "ms": fwd_ms, "bytes": f_bytes}
+    ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "KDA fwd+bwd tokens/s (H=32, d=128, T=8192)",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, kda_inputs workload 2)",
+        "config": {"workload": spec["name"], "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
+                   "global_batch": B, "seq_len": T, "state": "fp32", "outputs": "fp32"},
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_infer_ms": inf_ms,
+        "fwd_infer_tokens_per_s": tokens / (inf_ms * 1e-3),
+        "step_hbm_frac": fb_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None},
+        "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd_kernel (inference, no save)",
+                         "achieved": f_bytes / (inf_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None},
+        "timed_wall_s": wall,
+    }
+    if args.cpu_heads > 0:
+        line["cpu_baseline"] = cpu_baseline(x, cu, spec, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
