@@ -150,6 +150,30 @@ __device__ __forceinline__ int perm32(int k) {
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+
+// (I + N)^{-1} for one strictly lower-triangular 16x16 block N (fp32), by the
+// identity (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), with
+// fp32 MFMA.  Every matrix X is carried as the accumulator pair (X, X^T): the
+// accumulator layout of X is X's k16 B fragment and that of X^T is X's A
+// fragment, so no product needs a trip through LDS.
+// In: na[j] = N[cl][4qg+j] and nb[j] = N[4qg+j][cl].  Out: T[4qg+i][cl].
+__device__ __forceinline__ f32x4 inv_unit_lower16(f32x4 na, f32x4 nb, int qg, int cl) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = (4 * qg + i == cl) ? 1.f : 0.f;
+    const f32x4 p2 = mma_k16(z, na, nb);     // N.N
+    const f32x4 p2t = mma_k16(z, nb, na);    // N^T.N^T
+    const f32x4 p4 = mma_k16(z, p2t, p2);
+    const f32x4 p4t = mma_k16(z, p2, p2t);
+    const f32x4 p8 = mma_k16(z, p4t, p4);
+    const f32x4 y = mma_k16(eye + p4 + p8, p4t, p8);   // (I + P4)(I + P8)
+    const f32x4 zz = mma_k16(y, p2t, y);               // (I + P2) Y
+    return mma_k16(zz, -na, zz);                       // (I - N) Z
+}
+
 
 // ---------------------------------------------------- global loads/stores
 // Loads N consecutive elements of type T (N*sizeof(T) in {8,16,32} bytes)
@@ -179,6 +203,40 @@ __device__ __forceinline__ void gload(float (&dst)[N], const T* __restrict__ src
         }
     }
 }
+
+
+// A row piece of N input elements kept in registers in its storage format
+// (bf16 pairs packed two per register), widened to fp32 only when used.
+template <typename T, int N> struct RawRow;
+template <int N> struct RawRow<bf16, N> {
+    typedef unsigned short u16n __attribute__((ext_vector_type(N)));
+    u16n x;
+    __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const u16n*>(p); }
+    __device__ __forceinline__ void zero() { x = (u16n)0; }
+    __device__ __forceinline__ float operator[](int j) const { return __uint_as_float(((unsigned)x[j]) << 16); }
+};
+template <int N> struct RawRow<float, N> {
+    typedef float fn __attribute__((ext_vector_type(N)));
+    fn x;
+    __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const fn*>(p); }
+    __device__ __forceinline__ void zero() { x = (fn)0.f; }
+    __device__ __forceinline__ float operator[](int j) const { return x[j]; }
+};
+
+// One input scalar kept in storage format until used.
+template <typename T> struct RawScalar;
+template <> struct RawScalar<bf16> {
+    unsigned short x;
+    __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const unsigned short*>(p); }
+    __device__ __forceinline__ void zero() { x = 0; }
+    __device__ __forceinline__ float f() const { return __uint_as_float(((unsigned)x) << 16); }
+};
+template <> struct RawScalar<float> {
+    float x;
+    __device__ __forceinline__ void load(const float* p) { x = *p; }
+    __device__ __forceinline__ void zero() { x = 0.f; }
+    __device__ __forceinline__ float f() const { return x; }
+};
 
 template <typename T> __device__ __forceinline__ float gload1(const T* p) { return to_f32(*p); }
 

@@ -104,27 +104,41 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i)
             S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
 
-    // ---- raw chunk registers (prefetched one chunk ahead)
-    float rq[4][CPL], rk[4][CPL], rg[4][CPL], rv[4][VPL], rb[4];
+    // ---- raw chunk registers (prefetched one chunk ahead, kept in input format)
+    RawRow<T, CPL> rq[4], rk[4], rg[4];
+    RawRow<T, VPL> rv[4];
+    RawScalar<T> rb[4];
+    const int64_t rs_k = (int64_t)H * DK, rs_v = (int64_t)H * dv;   // token strides
     auto load_chunk = [&](int64_t c0) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+        const int r0 = 16 * w + 4 * qg;
+        const T* qc = qp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* kc = kp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* gc = gp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* vc = vp + (c0 + r0) * rs_v + h * dv + dv0 + VPL * cl;
+        const T* bc = bp + (c0 + r0) * H + h;
+        if (r0 + 4 <= L) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * qg + i;
-            if (r < L) {
-                const int64_t tok = c0 + r;
-                const int64_t rowk = (tok * H + h) * DK + CPL * cl;
-                gload<T, CPL>(rq[i], qp + rowk);
-                gload<T, CPL>(rk[i], kp + rowk);
-                gload<T, CPL>(rg[i], gp + rowk);
-                gload<T, VPL>(rv[i], vp + (tok * H + h) * dv + dv0 + VPL * cl);
-                rb[i] = gload1(bp + tok * H + h);
-            } else {
+            for (int i = 0; i < 4; ++i) {
+                rq[i].load(qc + i * rs_k);
+                rk[i].load(kc + i * rs_k);
+                rg[i].load(gc + i * rs_k);
+                rv[i].load(vc + i * rs_v);
+                rb[i].load(bc + i * H);
+            }
+        } else {
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) { rq[i][e] = 0.f; rk[i][e] = 0.f; rg[i][e] = 0.f; }
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) rv[i][e] = 0.f;
-                rb[i] = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                if (r0 + i < L) {
+                    rq[i].load(qc + i * rs_k);
+                    rk[i].load(kc + i * rs_k);
+                    rg[i].load(gc + i * rs_k);
+                    rv[i].load(vc + i * rs_v);
+                    rb[i].load(bc + i * H);
+                } else {
+                    rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
+                    rb[i].zero();
+                }
             }
         }
     };
@@ -153,15 +167,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
             nq[i] = sqrtf(sq + p.eps);
             nk[i] = sqrtf(sk + p.eps);
             const int r = 16 * w + 4 * qg + i;
-            beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
+            beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i].f())) : 0.f;
         }
-        // inclusive cumulative sum of g over the chunk rows
+        // inclusive cumulative sum of g over the chunk rows, in log2 units
         float G[4][CPL];
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
             float a = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { a += rg[i][e]; G[i][e] = a; }
+            for (int i = 0; i < 4; ++i) { a += rg[i][e] * kLog2e; G[i][e] = a; }
             const float tot = a;
             float s = tot, x;
             x = __shfl_up(s, 16);
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
         }
         if (w == 0 && qg == 0) {
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = fast_exp(GC[e]);
+            for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = fast_exp2(GC[e]);
         }
         if (cl == 0) {
 #pragma unroll
@@ -207,25 +221,22 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
                 }
             }
         }
-        // operand tiles
-        float ktv[CPL][4];
+        // operand tiles: qh Gam, beta kh Gam, kh / Gam
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * w + 4 * qg + i;
-            const float iq = p.scale / nq[i], ik = 1.f / nk[i];
+            const float aq = p.scale / nq[i], ai = 1.f / nk[i], ak = beta[i] * ai;
 #pragma unroll
             for (int e4 = 0; e4 < CPL; e4 += 4) {
                 f32x4 vq, vk, vi;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int e = e4 + j;
-                    const float kh = rk[i][e] * ik;
-                    const float gam = fast_exp(G[i][e]);
-                    const float gin = fast_exp(-G[i][e]);
-                    vq[j] = rq[i][e] * iq * gam;
-                    vk[j] = beta[i] * kh * gam;
-                    vi[j] = kh * gin;
-                    ktv[e][i] = kh * fast_exp(GC[e] - G[i][e]);
+                    const float gam = fast_exp2(G[i][e]);
+                    const float gin = fast_exp2(-G[i][e]);
+                    vq[j] = (rq[i][e] * aq) * gam;
+                    vk[j] = (rk[i][e] * ak) * gam;
+                    vi[j] = (rk[i][e] * ai) * gin;
                 }
                 const int pc = perm32(CPL * cl + e4);
                 sts4_split<T, SPLIT>(&sm.qg[r * PK + pc], &sm.qgl[SPLIT ? r * PK + pc : 0], vq);
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 
         // ================= intra: Akk, Aqk =================
         {
-#pragma unroll
+#pragma unroll 1
             for (int st = 0; st < 5; ++st) {
                 const int it = w + 4 * st;          // 0..9: Akk blocks, 10..19: Aqk blocks
                 const bool isqk = it >= 10;
@@ -284,20 +295,33 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
                 }
             }
         }
+        // Ktil = kh Gam_C / Gam = (kh/Gam) * Gam_C, from the hi+lo tiles (read
+        // before the barrier: the lo tile is overwritten right after it)
+        float ktv[CPL][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * qg + i;
+#pragma unroll
+            for (int e4 = 0; e4 < CPL; e4 += 4) {
+                const int pc = perm32(CPL * cl + e4);
+                f32x4 x = lds4f<T>(&sm.ki[r * PK + pc]);
+                if constexpr (SPLIT) x += lds4f<T>(&sm.kil[r * PK + pc]);
+                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[CPL * cl + e4]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ktv[e4 + j][i] = x[j] * gcv[j];
+            }
+        }
         __syncthreads();
 
-        // ======== (I + Akk_ww)^{-1}: forward substitution, column cl ========
-        if (l < 16) {
-            float x[16];
+        // ======== (I + Akk_ww)^{-1} for diagonal block w ========
+        {
+            const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[w][cl][4 * qg]);
+            f32x4 nb;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == l) ? 1.f : 0.f;
+            for (int j = 0; j < 4; ++j) nb[j] = sm.adiag[w][4 * qg + j][cl];
+            const f32x4 tw = inv_unit_lower16(na, nb, qg, cl);
 #pragma unroll
-                for (int c = 0; c < r; ++c) s -= sm.adiag[w][r][c] * x[c];
-                x[r] = s;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.tdiag[w][r][l] = x[r];
+            for (int i = 0; i < 4; ++i) sm.tdiag[w][4 * qg + i][cl] = tw[i];
         }
         // Ktil^T tiles: the lo part goes where kh/Gam lo lived (read only by intra)
         {
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
         split8<T, SPLIT>(U[0], U[1], ufh[0], ufl[0]);
         split8<T, SPLIT>(U[2], U[3], ufh[1], ufl[1]);
         // O = (qh Gam) S + Aqk U
-#pragma unroll
+#pragma unroll 2
         for (int i = 0; i < 4; ++i) {
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
             const int ro = (16 * i + cl) * PK + 8 * qg, ra = (16 * i + cl) * PC + 8 * qg;
