@@ -384,11 +384,796 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_scan_kernel(BwdParams p) 
 // ============================================================================
 // B2: chunk-parallel gradients
 // ============================================================================
-// Every matrix lives in LDS in fp32; an MFMA operand fragment (8 values along
-// the contraction index) is gathered in whichever orientation the product
-// needs, split into bf16 hi + lo, and contracted with three k32 MFMAs
-// (hi.hi + hi.lo + lo.hi), which keeps about 16 mantissa bits per operand.
+// One workgroup per (chunk, head), full value width.  Operand tiles live in LDS
+// in the orientation each product contracts over (8 contiguous elements per
+// lane), written once per chunk; bf16 operands whose rounding shows in a
+// gradient carry a lo tile and take three MFMAs.  The fp32 entering state S0
+// and dS1 feed B fragments straight from global memory.  dU, dT and dW act as
+// accumulator-resident B operands of the T^T products (perm32 layout of T^T).
 
+__device__ __forceinline__ void st_blk(float* M, int ld, int m0, int n0, f32x4 x, int qg, int cl) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[(m0 + 4 * qg + i) * ld + n0 + cl] = x[i];
+}
+
+// Find the sequence that owns state slot `slot` (slot = floor(cu[n]/64) + n + j).
+__device__ __forceinline__ int slot_owner(const int32_t* cu, int N, int seqlen, int64_t slot) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int64_t start = cu ? (int64_t)cu[mid] : (int64_t)mid * seqlen;
+        if (start / kChunk + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Slot layout of the chunk kernel's LDS (bytes).
+template <typename T, int DK, int DV>
+struct ChunkLds {
+    static constexpr int PK = DK + 8, PV = DV + 8, PC = kChunk + 8, PF = kChunk + 4;
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int RK = kChunk * PK * ES;          // [64][DK] tile
+    static constexpr int RV = kChunk * PV * ES;          // [64][DV] tile
+    static constexpr int CK = DK * PC * ES;              // [DK][64] tile
+    static constexpr int CV = DV * PC * ES;              // [DV][64] tile
+    static constexpr int RQ = kChunk * PC * ES;          // [64][64] tile
+    static constexpr int FQ = kChunk * PF * 4;           // [64][64] fp32
+    static constexpr int m2(int a, int b) { return a > b ? a : b; }
+    static constexpr int SLOT0 = m2(m2(RK, RV), m2(CK, CV));
+    static constexpr int SLOT1 = m2(SLOT0, m2(2 * RQ, FQ));
+    static constexpr int SLOT = (SLOT1 + 255) & ~255;
+    static constexpr int NSLOT = 8;
+    static constexpr int QX = NSLOT * SLOT;              // one extra [64][64] tile
+    static constexpr int SMALL = QX + ((RQ + 255) & ~255);
+    // small arrays
+    static constexpr int BETA = SMALL;                   // float[64]
+    static constexpr int GC = BETA + 64 * 4;             // float[DK]
+    static constexpr int DGC = GC + DK * 4;              // float[DK]
+    static constexpr int RED = DGC + DK * 4;             // float[4][DK]
+    static constexpr int DBV = RED + 4 * DK * 4;         // float[4][64]
+    static constexpr int BYTES = DBV + 4 * 64 * 4;
+    static_assert(BYTES <= 163840, "chunk kernel LDS");
+};
+
+// --- fragment helpers ------------------------------------------------------
+// 8 fp32 values -> bf16 hi (and lo) fragments
+__device__ __forceinline__ void cvt8(const float (&x)[8], bf16x8& hi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hi[j] = (bf16)x[j];
+}
+__device__ __forceinline__ void cvt8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        hi[j] = (bf16)x[j];
+        lo[j] = (bf16)(x[j] - (float)hi[j]);
+    }
+}
+__device__ __forceinline__ void cvt8(const float (&x)[8], f32x8& hi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hi[j] = x[j];
+}
+__device__ __forceinline__ void cvt8(const float (&x)[8], f32x8& hi, f32x8& lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { hi[j] = x[j]; lo[j] = 0.f; }
+}
+// 8 contiguous fp32 from global
+__device__ __forceinline__ void gf8(float (&x)[8], const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+// 8 strided fp32 from global
+__device__ __forceinline__ void gs8(float (&x)[8], const float* p, int ld) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = p[(int64_t)j * ld];
+}
+// 8 contiguous input elements from global as an operand fragment (exact)
+__device__ __forceinline__ bf16x8 gin8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 gin8(const float* p) {
+    f32x8 r;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+    return r;
+}
+
+// Store an accumulator block (rows m0+4qg+i, col n0+cl) into a tile.
+// RM: row-major tile [m][n] (stride ld); else transposed tile [n][m].
+template <typename T, bool SPLIT>
+__device__ __forceinline__ void put_blk(T* hi, T* lo, int ld, int m0, int n0, f32x4 x, int qg, int cl, bool rm) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int o = rm ? (m0 + 4 * qg + i) * ld + n0 + cl : (n0 + cl) * ld + m0 + 4 * qg + i;
+        const T h = from_f32<T>(x[i]);
+        hi[o] = h;
+        if constexpr (SPLIT) lo[o] = from_f32<T>(x[i] - to_f32(h));
+    }
+}
+// Transposed store of 4 consecutive rows as one vector, tile [n][m] with m permuted by perm32.
+template <typename T, bool SPLIT>
+__device__ __forceinline__ void put_blk_tp(T* hi, T* lo, int ld, int m0, int n0, f32x4 x, int qg, int cl) {
+    const int o = (n0 + cl) * ld + perm32(m0 + 4 * qg);
+    sts4_split<T, SPLIT>(hi + o, lo + (SPLIT ? o : 0), x);
+}
+
+template <typename T, typename TO, int DK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p) {
+    typedef ChunkLds<T, DK, DV> LY;
+    __shared__ __attribute__((aligned(256))) char lds[LY::BYTES];
+    constexpr bool SPLIT = std::is_same<T, bf16>::value;
+    constexpr int PK = LY::PK, PV = LY::PV, PC = LY::PC, PF = LY::PF;
+    constexpr int CPL = DK / 16, VPL = DV / 16;
+    constexpr int NBK = DK / 64, NBV = DV / 64;     // column blocks per wave (dk- / dv-wide outputs)
+    constexpr int NKK = DK / 32, NKV = DV / 32;     // k32 steps over dk / dv
+    typedef typename V8<T>::t V8T;
+    auto S = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT); };
+    auto Sh = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT + LY::RQ); };   // second half
+    auto Sf = [&](int i) { return reinterpret_cast<float*>(lds + i * LY::SLOT); };
+    T* const QX = reinterpret_cast<T*>(lds + LY::QX);
+    float* const sbeta = reinterpret_cast<float*>(lds + LY::BETA);
+    float* const sgc = reinterpret_cast<float*>(lds + LY::GC);
+    float* const sdgc = reinterpret_cast<float*>(lds + LY::DGC);
+    float* const sred = reinterpret_cast<float*>(lds + LY::RED);
+    float* const sdbv = reinterpret_cast<float*>(lds + LY::DBV);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const int H = p.H;
+    const int64_t slot = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    const int n = slot_owner(p.cu, p.N, p.seqlen, slot);
+    int64_t t0, t1;
+    seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
+    const int64_t jc = slot - (t0 / kChunk + n);
+    const int64_t c0 = t0 + jc * kChunk;
+    if (jc < 0 || c0 >= t1) return;   // unused slot (uniform across the workgroup)
+    const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+
+    const int64_t rsk = (int64_t)H * DK, rsv = (int64_t)H * DV;   // token strides
+    const T* __restrict__ qc = reinterpret_cast<const T*>(p.q) + c0 * rsk + h * DK;
+    const T* __restrict__ kc = reinterpret_cast<const T*>(p.k) + c0 * rsk + h * DK;
+    const T* __restrict__ gcp = reinterpret_cast<const T*>(p.g) + c0 * rsk + h * DK;
+    const T* __restrict__ vc = reinterpret_cast<const T*>(p.v) + c0 * rsv + h * DV;
+    const T* __restrict__ doc = reinterpret_cast<const T*>(p.dO) + c0 * rsv + h * DV;
+    const T* __restrict__ bc = reinterpret_cast<const T*>(p.b) + c0 * H + h;
+    const float* __restrict__ S0 = reinterpret_cast<const float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
+    const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // ================= prep (rows 16w+4qg+i, key cols CPL*cl+e) =================
+    RawRow<T, CPL> rq[4], rk[4];
+    float G[4][CPL], beta[4], nq[4], nk[4], GC[CPL];
+    {
+        RawRow<T, CPL> rg[4];
+        float rb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * qg + i;
+            if (r < L) {
+                rq[i].load(qc + r * rsk + CPL * cl);
+                rk[i].load(kc + r * rsk + CPL * cl);
+                rg[i].load(gcp + r * rsk + CPL * cl);
+                rb[i] = gload1(bc + (int64_t)r * H);
+                nq[i] = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
+                nk[i] = p.nk_saved[(c0 + r) * H + h];
+            } else {
+                rq[i].zero(); rk[i].zero(); rg[i].zero();
+                rb[i] = 0.f; nq[i] = 1.f; nk[i] = 1.f;
+            }
+            beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { a += rg[i][e] * kLog2e; G[i][e] = a; }
+            const float tot = a;
+            float s = tot, x;
+            x = __shfl_up(s, 16);
+            if (qg >= 1) s += x;
+            x = __shfl_up(s, 32);
+            if (qg >= 2) s += x;
+            const float excl = s - tot;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[i][e] += excl;
+            if (qg == 3) sred[w * DK + CPL * cl + e] = s;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+        const int c = CPL * cl + e;
+        float a = 0.f, tot = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float x = sred[ww * DK + c];
+            if (ww < w) a += x;
+            tot += x;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G[i][e] += a;
+        GC[e] = tot;
+    }
+    if (w == 0 && qg == 0) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) sgc[CPL * cl + e] = fast_exp2(GC[e]);
+    }
+    if (cl == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sbeta[16 * w + 4 * qg + i] = beta[i];
+    }
+    // prep-layout value of qh*Gam, beta*kh*Gam, kh/Gam, Ktil at (row i, col e)
+    auto vQG = [&](int i, int e) { return rq[i][e] * (p.scale / nq[i]) * fast_exp2(G[i][e]); };
+    auto vKG = [&](int i, int e) { return rk[i][e] * (beta[i] / nk[i]) * fast_exp2(G[i][e]); };
+    auto vKI = [&](int i, int e) { return rk[i][e] * (1.f / nk[i]) * fast_exp2(-G[i][e]); };
+    auto vKt = [&](int i, int e) { return rk[i][e] * (1.f / nk[i]) * fast_exp2(GC[e] - G[i][e]); };
+    // writers: row-major [r][c] tile (stride PK) or transposed [c][perm32(r)] tile (stride PC)
+    auto put_rm = [&](T* hi, T* lo, auto val, bool split) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * qg + i;
+#pragma unroll
+            for (int e4 = 0; e4 < CPL; e4 += 4) {
+                f32x4 x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = val(i, e4 + j);
+                const int o = r * PK + CPL * cl + e4;
+                if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
+                else sts4<T>(hi + o, x);
+            }
+        }
+    };
+    auto put_tp = [&](T* hi, T* lo, auto val, bool split, bool perm) {
+        const int r0 = 16 * w + 4 * qg;
+        const int pr = perm ? perm32(r0) : r0;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            f32x4 x = {val(0, e), val(1, e), val(2, e), val(3, e)};
+            const int o = (CPL * cl + e) * PC + pr;
+            if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
+            else sts4<T>(hi + o, x);
+        }
+    };
+    put_rm(S(0), S(1), vQG, true);    // QG  h/l
+    put_rm(S(2), S(3), vKI, true);    // KI  h/l
+    put_rm(S(4), S(4), vKG, false);   // KG  h
+    __syncthreads();
+
+    // ================= Akk (fp32 -> slot 5), Aqk^T h/l (slot 6) =================
+    float* const Af = Sf(5);
+    {
+        const int nb = 16 * w;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 a = zero, b = zero;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int ka = (16 * mb + cl) * PK + 32 * kk + 8 * qg, kb = (nb + cl) * PK + 32 * kk + 8 * qg;
+                const V8T ki_h = lds8<T>(S(2) + kb);
+                a = mma_k32(a, lds8<T>(S(4) + ka), ki_h);
+                b = mma3<SPLIT>(b, lds8<T>(S(0) + ka), lds8<T>(S(1) + ka), ki_h, lds8<T>(S(3) + kb));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mb + 4 * qg + i, s = nb + cl;
+                a[i] = s < r ? a[i] : 0.f;
+                b[i] = s <= r ? b[i] : 0.f;
+                Af[r * PF + s] = a[i];
+            }
+            // Aqk^T tile [s][r] (plain index order)
+            put_blk<T, SPLIT>(S(6), Sh(6), PC, 16 * mb, nb, b, qg, cl, false);
+        }
+    }
+    __syncthreads();
+    // ================= T = (I + Akk)^{-1} (fp32 in slot 7) =================
+    float* const Tf = Sf(7);
+    {
+        const f32x4 na = *reinterpret_cast<const f32x4*>(&Af[(16 * w + cl) * PF + 16 * w + 4 * qg]);
+        f32x4 nbv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nbv[j] = Af[(16 * w + 4 * qg + j) * PF + 16 * w + cl];
+        const f32x4 tw = inv_unit_lower16(na, nbv, qg, cl);
+        for (int e = tid; e < kChunk * PF; e += kThreads) {
+            const int r = e / PF, c = e % PF;
+            if ((r >> 4) != (c >> 4) || c >= kChunk) Tf[e] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Tf[(16 * w + 4 * qg + i) * PF + 16 * w + cl] = tw[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        // tmp_ij = sum_{k=j}^{i-1} Akk_ik T_kj in the (unused) upper block (j, i) of Af
+        for (int idx = tid; idx < (4 - d) * 256; idx += kThreads) {
+            const int j = idx >> 8, i = j + d, a = (idx >> 4) & 15, bb = idx & 15;
+            float s = 0.f;
+            for (int k = j; k < i; ++k)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) s += Af[(16 * i + a) * PF + 16 * k + t] * Tf[(16 * k + t) * PF + 16 * j + bb];
+            Af[(16 * j + a) * PF + 16 * i + bb] = s;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < (4 - d) * 256; idx += kThreads) {
+            const int j = idx >> 8, i = j + d, a = (idx >> 4) & 15, bb = idx & 15;
+            float s = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s += Tf[(16 * i + a) * PF + 16 * i + t] * Af[(16 * j + t) * PF + 16 * i + bb];
+            Tf[(16 * i + a) * PF + 16 * j + bb] = -s;
+        }
+        __syncthreads();
+    }
+    // T tiles: Trm [r][s] (slot 5 first half), T diag(beta) [r][s] h/l (slot 5 second half, slot 0
+    // second half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1); V^T, dO^T [j][r] (slots 2, 3)
+    {
+        T* const Trm = S(5);
+        T* const Tb = Sh(5);
+        T* const Tbl = Sh(0);
+        T* const Ttp = S(0);
+        for (int e = tid; e < kChunk * kChunk; e += kThreads) {
+            const int r = e >> 6, c = e & 63;
+            const float t = Tf[r * PF + c];
+            Trm[r * PC + c] = from_f32<T>(t);
+            // the diagonal of T diag(beta) is beta itself: its rounding would show in U
+            const float tb = t * sbeta[c];
+            const T tbh = from_f32<T>(tb);
+            Tb[r * PC + c] = tbh;
+            if constexpr (SPLIT) Tbl[r * PC + c] = from_f32<T>(tb - to_f32(tbh));
+            Ttp[c * PC + perm32(r)] = from_f32<T>(t);
+        }
+        put_tp(S(1), S(1), vKG, false, false);
+        const int r0 = 16 * w + 4 * qg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            RawRow<T, VPL> vv, dd;
+            if (r < L) { vv.load(vc + r * rsv + VPL * cl); dd.load(doc + r * rsv + VPL * cl); }
+            else { vv.zero(); dd.zero(); }
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) {
+                S(2)[(VPL * cl + e) * PC + r] = from_f32<T>(vv[e]);
+                S(3)[(VPL * cl + e) * PC + r] = from_f32<T>(dd[e]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ================= W = T KG, Ut = T diag(beta) v =================
+    f32x4 Wc[NBK][4], U[NBV][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int t = 0; t < NBK; ++t) {
+            f32x4 a = zero;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                a = mma_k32(a, lds8<T>(S(5) + (16 * mb + cl) * PC + 32 * kk + 8 * qg),
+                            lds8<T>(S(1) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg));
+            Wc[t][mb] = a;
+        }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int t = 0; t < NBV; ++t) {
+            f32x4 a = zero;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg;
+                const V8T bv = lds8<T>(S(2) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg);
+                a = mma_k32(a, lds8<T>(Sh(5) + ka), bv);
+                if constexpr (SPLIT) a = mma_k32(a, lds8<T>(Sh(0) + ka), bv);
+            }
+            U[t][mb] = a;
+        }
+    __syncthreads();
+    // W rm (slot 4), Ktil rm h/l (slots 7, 2)
+#pragma unroll
+    for (int t = 0; t < NBK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(4), S(4), PK, 16 * mb, 16 * (w + 4 * t), Wc[t][mb], qg, cl, true);
+    put_rm(S(7), S(2), vKt, true);
+    __syncthreads();
+    // ================= U = Ut - W S0;  dU = Aqk^T dO + Ktil dS1 =================
+    f32x4 dU[NBV][4];
+#pragma unroll
+    for (int t = 0; t < NBV; ++t) {
+        const int nc = 16 * (w + 4 * t) + cl;   // value column of this lane's B fragments
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            float x[8];
+            V8T bs, bd, bdl;
+            gs8(x, S0 + (int64_t)(32 * kk + 8 * qg) * DV + nc, DV);
+            cvt8(x, bs);
+            gs8(x, dS1 + (int64_t)(32 * kk + 8 * qg) * DV + nc, DV);
+            if constexpr (SPLIT) cvt8(x, bd, bdl); else cvt8(x, bd);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int ka = (16 * mb + cl) * PK + 32 * kk + 8 * qg;
+                f32x4 uu = mma_k32(zero, lds8<T>(S(4) + ka), bs);
+                U[t][mb] -= uu;
+                if (kk == 0) dU[t][mb] = zero;
+                dU[t][mb] = mma3<SPLIT>(dU[t][mb], lds8<T>(S(7) + ka), lds8<T>(S(2) + (SPLIT ? ka : 0)), bd, SPLIT ? bdl : bd);
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg;
+                const V8T bo = lds8<T>(S(3) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg);
+                dU[t][mb] = mma_k32(dU[t][mb], lds8<T>(S(6) + ka), bo);
+                if constexpr (SPLIT) dU[t][mb] = mma_k32(dU[t][mb], lds8<T>(Sh(6) + ka), bo);
+            }
+    }
+    __syncthreads();
+    // U rm h/l (slots 4, 3), dU rm (slot 7)
+#pragma unroll
+    for (int t = 0; t < NBV; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * (w + 4 * t), U[t][mb], qg, cl, true);
+            put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * (w + 4 * t), dU[t][mb], qg, cl, true);
+        }
+    __syncthreads();
+
+    // ================= dBV = T^T dU  ->  dv, dbeta (v part) =================
+    {
+        TO* __restrict__ dvp = reinterpret_cast<TO*>(p.dv_out) + c0 * rsv + h * DV;
+        float rowpart[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rowpart[mb][i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NBV; ++t) {
+            V8T bh[2], bl[2];
+            split8<T, SPLIT>(dU[t][0], dU[t][1], bh[0], bl[0]);
+            split8<T, SPLIT>(dU[t][2], dU[t][3], bh[1], bl[1]);
+            const int nc = 16 * (w + 4 * t) + cl;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                f32x4 a = zero;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const V8T ah = lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
+                    a = mma_k32(a, ah, bh[kk]);
+                    if constexpr (SPLIT) a = mma_k32(a, ah, bl[kk]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mb + 4 * qg + i;
+                    if (r < L) {
+                        dvp[r * rsv + nc] = from_f32<TO>(sbeta[r] * a[i]);
+                        rowpart[mb][i] += gload1(vc + r * rsv + nc) * a[i];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = rowpart[mb][i];
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) s += __shfl_xor(s, m);
+                if (cl == 0) sdbv[w * 64 + 16 * mb + 4 * qg + i] = s;
+            }
+    }
+    // ================= dAqk = lower(dO U^T);  dT = (dU v^T) diag(beta) =================
+    f32x4 dAqk[4], dT[4];
+    {
+        const int nb = 16 * w;
+        const bool rowok = nb + cl < L;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) { dAqk[mb] = zero; dT[mb] = zero; }
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            const int kb = (nb + cl) * PV + 32 * kk + 8 * qg;
+            const V8T uh = lds8<T>(S(4) + kb), ul = lds8<T>(S(3) + (SPLIT ? kb : 0));
+            V8T vb;
+            if (rowok) vb = gin8(vc + (nb + cl) * rsv + 32 * kk + 8 * qg);
+            else vb = V8T{};
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int r = 16 * mb + cl;
+                V8T da;
+                if (r < L) da = gin8(doc + r * rsv + 32 * kk + 8 * qg);
+                else da = V8T{};
+                dAqk[mb] = mma_k32(dAqk[mb], da, uh);
+                if constexpr (SPLIT) dAqk[mb] = mma_k32(dAqk[mb], da, ul);
+                dT[mb] = mma_k32(dT[mb], lds8<T>(S(7) + (16 * mb + cl) * PV + 32 * kk + 8 * qg), vb);
+            }
+        }
+        const float bs = sbeta[nb + cl];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mb + 4 * qg + i;
+                dAqk[mb][i] = nb + cl <= r ? dAqk[mb][i] : 0.f;
+                dT[mb][i] *= bs;
+            }
+    }
+    // ================= dQG = dO S0^T;  dW = -dU S0^T;  dKt = U dS1^T =================
+    f32x4 dQG[NBK][4], dW[NBK][4], dKt[NBK][4];
+#pragma unroll
+    for (int t = 0; t < NBK; ++t) {
+        const int nr = 16 * (w + 4 * t) + cl;   // key row of S0 / dS1 feeding this lane
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) { dQG[t][mb] = zero; dW[t][mb] = zero; dKt[t][mb] = zero; }
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            float x[8];
+            V8T sh, sl, dh, dl;
+            gf8(x, S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            if constexpr (SPLIT) cvt8(x, sh, sl); else cvt8(x, sh);
+            gf8(x, dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            if constexpr (SPLIT) cvt8(x, dh, dl); else cvt8(x, dh);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int r = 16 * mb + cl;
+                V8T da;
+                if (r < L) da = gin8(doc + r * rsv + 32 * kk + 8 * qg);
+                else da = V8T{};
+                dQG[t][mb] = mma_k32(dQG[t][mb], da, sh);
+                if constexpr (SPLIT) dQG[t][mb] = mma_k32(dQG[t][mb], da, sl);
+                const int ka = r * PV + 32 * kk + 8 * qg;
+                dW[t][mb] = mma_k32(dW[t][mb], lds8<T>(S(7) + ka), sh);
+                dKt[t][mb] = mma3<SPLIT>(dKt[t][mb], lds8<T>(S(4) + ka), lds8<T>(S(3) + (SPLIT ? ka : 0)), dh,
+                                         SPLIT ? dl : dh);
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) dW[t][mb] = -dW[t][mb];
+    }
+    {
+        // dL/dGam_C[c] = sum_j S0[c][j] dS1[c][j]
+        constexpr int TPR = kThreads / DK;
+        const int c = tid / TPR, part = tid % TPR;
+        float s = 0.f;
+        for (int j = part * 4; j < DV; j += TPR * 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + j);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(dS1 + (int64_t)c * DV + j);
+            s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+        }
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
+        if (part == 0) sdgc[c] = s;
+    }
+    __syncthreads();
+    // dW rm (slot 2), KG rm (slot 6)
+#pragma unroll
+    for (int t = 0; t < NBK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(2), S(2), PK, 16 * mb, 16 * (w + 4 * t), dW[t][mb], qg, cl, true);
+    put_rm(S(6), S(6), vKG, false);
+    __syncthreads();
+    // ================= dT += dW KG^T;  X = T^T dT -> slot 0 (2nd half) =================
+    {
+        const int nb = 16 * w;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const V8T bk = lds8<T>(S(6) + (nb + cl) * PK + 32 * kk + 8 * qg);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                dT[mb] = mma_k32(dT[mb], lds8<T>(S(2) + (16 * mb + cl) * PK + 32 * kk + 8 * qg), bk);
+        }
+        V8T th[2], tl[2];
+        split8<T, false>(dT[0], dT[1], th[0], tl[0]);
+        split8<T, false>(dT[2], dT[3], th[1], tl[1]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 x = zero;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) x = mma_k32(x, lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg), th[kk]);
+            put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, x, qg, cl, true);
+        }
+    }
+    __syncthreads();
+    // ================= dAkk = -strict(X T^T) =================
+    f32x4 dAkk[4];
+    {
+        const int nb = 16 * w;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 a = zero;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                a = mma_k32(a, lds8<T>(Sh(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg),
+                            lds8<T>(S(5) + (nb + cl) * PC + 32 * kk + 8 * qg));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mb + 4 * qg + i;
+                a[i] = nb + cl < r ? -a[i] : 0.f;
+            }
+            dAkk[mb] = a;
+        }
+    }
+    __syncthreads();
+    // tiles for the last products:
+    //   dAkk rm [r][s] (slot 0, 2nd half), dAkk^T [s][r] (QX), dAqk rm h/l (slot 3),
+    //   dAqk^T h/l (slot 7), KI^T h/l [c][s] (slots 2, 6), QG^T h/l [c][r] (slots 4, 5)
+    {
+        const int nb = 16 * w;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, dAkk[mb], qg, cl, true);
+            put_blk<T, false>(QX, QX, PC, 16 * mb, nb, dAkk[mb], qg, cl, false);
+            put_blk<T, SPLIT>(S(3), Sh(3), PC, 16 * mb, nb, dAqk[mb], qg, cl, true);
+            put_blk<T, SPLIT>(S(7), Sh(7), PC, 16 * mb, nb, dAqk[mb], qg, cl, false);
+        }
+        put_tp(S(2), S(6), vKI, true, false);
+        put_tp(S(4), S(5), vQG, true, false);
+    }
+    __syncthreads();
+    // ================= dKG = T^T dW + dAkk KI;  dQG += dAqk KI;  dKI = dAkk^T KG + dAqk^T QG =================
+    f32x4 dKG[NBK][4], dKI[NBK][4];
+#pragma unroll
+    for (int t = 0; t < NBK; ++t) {
+        const int nb = 16 * (w + 4 * t);
+        V8T wh[2], wl[2];
+        split8<T, false>(dW[t][0], dW[t][1], wh[0], wl[0]);
+        split8<T, false>(dW[t][2], dW[t][3], wh[1], wl[1]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 a = zero, qq = dQG[t][mb], ki = zero;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = (nb + cl) * PC + 32 * kk + 8 * qg;
+                a = mma_k32(a, lds8<T>(S(0) + ka), wh[kk]);                                  // T^T dW
+                const V8T kih = lds8<T>(S(2) + kb);
+                a = mma_k32(a, lds8<T>(Sh(0) + ka), kih);                                    // dAkk KI
+                qq = mma3<SPLIT>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + (SPLIT ? ka : 0)), kih,
+                                 lds8<T>(S(6) + (SPLIT ? kb : 0)));                          // dAqk KI
+                ki = mma_k32(ki, lds8<T>(QX + ka), lds8<T>(S(1) + kb));                      // dAkk^T KG
+                ki = mma3<SPLIT>(ki, lds8<T>(S(7) + ka), lds8<T>(Sh(7) + (SPLIT ? ka : 0)), lds8<T>(S(4) + kb),
+                                 lds8<T>(S(5) + (SPLIT ? kb : 0)));                          // dAqk^T QG
+            }
+            dKG[t][mb] = a;
+            dQG[t][mb] = qq;
+            dKI[t][mb] = ki;
+        }
+    }
+    __syncthreads();
+
+    // ================= back to the prep layout (fp32 through LDS) =================
+    constexpr int LDF = DK + 4;
+    float* const F0 = Sf(0);   // slots 0-1
+    float* const F1 = Sf(2);   // slots 2-3
+    float* const F2 = Sf(4);   // slots 4-5
+    static_assert(kChunk * LDF * 4 <= 2 * LY::SLOT, "fp32 staging");
+    float gQ[4][CPL], gKG[4][CPL], gKI[4][CPL], gKt[4][CPL];
+#pragma unroll
+    for (int t = 0; t < NBK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int nb = 16 * (w + 4 * t);
+            st_blk(F0, LDF, 16 * mb, nb, dQG[t][mb], qg, cl);
+            st_blk(F1, LDF, 16 * mb, nb, dKG[t][mb], qg, cl);
+            st_blk(F2, LDF, 16 * mb, nb, dKI[t][mb], qg, cl);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int o = (16 * w + 4 * qg + i) * LDF + CPL * cl + e;
+            gQ[i][e] = F0[o];
+            gKG[i][e] = F1[o];
+            gKI[i][e] = F2[o];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NBK; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) st_blk(F0, LDF, 16 * mb, 16 * (w + 4 * t), dKt[t][mb], qg, cl);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) gKt[i][e] = F0[(16 * w + 4 * qg + i) * LDF + CPL * cl + e];
+
+    // ================= chain rule to qh, kh, beta, G =================
+    float dqh[4][CPL], dkh[4][CPL], dG[4][CPL], dbk[4], colp[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) colp[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dbk[i] = 0.f;
+        const float aq = p.scale / nq[i], ai = 1.f / nk[i];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const float gam = fast_exp2(G[i][e]), gin = fast_exp2(-G[i][e]), ek = fast_exp2(GC[e] - G[i][e]);
+            const float qh = rq[i][e] * aq, kh = rk[i][e] * ai;
+            const float QG = qh * gam, KGv = beta[i] * kh * gam, KIv = kh * gin, Ktv = kh * ek;
+            dqh[i][e] = gQ[i][e] * gam;
+            dkh[i][e] = beta[i] * gam * gKG[i][e] + gKI[i][e] * gin + gKt[i][e] * ek;
+            dG[i][e] = gQ[i][e] * QG + gKG[i][e] * KGv - gKI[i][e] * KIv - gKt[i][e] * Ktv;
+            dbk[i] += gKG[i][e] * kh * gam;
+            colp[e] += gKt[i][e] * Ktv;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+        float s = colp[e];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (qg == 0) sred[w * DK + CPL * cl + e] = s;
+    }
+    __syncthreads();
+    float dGC[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+        const int c = CPL * cl + e;
+        dGC[e] = sred[c] + sred[DK + c] + sred[2 * DK + c] + sred[3 * DK + c] + sdgc[c] * sgc[c];
+    }
+    __syncthreads();
+    {
+        float suf[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) { a += dG[i][e]; dG[i][e] = a; }
+            const float tot = a;
+            float s = tot, x;
+            x = __shfl_down(s, 16);
+            if (qg <= 2) s += x;
+            x = __shfl_down(s, 32);
+            if (qg <= 1) s += x;
+            suf[e] = s - tot;
+            if (qg == 0) sred[w * DK + CPL * cl + e] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int c = CPL * cl + e;
+            float a = suf[e] + dGC[e];
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww)
+                if (ww > w) a += sred[ww * DK + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dG[i][e] += a;
+        }
+    }
+    // ================= through the L2 norms and the sigmoid; write =================
+    TO* __restrict__ dqp = reinterpret_cast<TO*>(p.dq) + c0 * rsk + h * DK;
+    TO* __restrict__ dkp = reinterpret_cast<TO*>(p.dk) + c0 * rsk + h * DK;
+    TO* __restrict__ dgp = reinterpret_cast<TO*>(p.dg) + c0 * rsk + h * DK;
+    TO* __restrict__ dbp = reinterpret_cast<TO*>(p.db) + c0 * H + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * qg + i;
+        const float aq = p.scale / nq[i], ai = 1.f / nk[i];
+        float sq = 0.f, sk = 0.f, db = dbk[i];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * aq * dqh[i][e]; sk += rk[i][e] * ai * dkh[i][e]; }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); db += __shfl_xor(db, m); }
+        if (r < L) {
+            const float sc = p.scale;
+            const float qdot = sc != 0.f ? sq / (sc * sc) : 0.f;   // (qh . dqh) / scale^2
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int64_t off = r * rsk + CPL * cl + e;
+                const float qh = rq[i][e] * aq, kh = rk[i][e] * ai;
+                dqp[off] = from_f32<TO>(aq * (dqh[i][e] - qh * qdot));
+                dkp[off] = from_f32<TO>(ai * (dkh[i][e] - kh * sk));
+                dgp[off] = from_f32<TO>(dG[i][e]);
+            }
+            if (cl == 0) {
+                const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
+                dbp[(int64_t)r * H] = from_f32<TO>(dbeta * beta[i] * (1.f - beta[i]));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32-input variant of B2: fp32 operands in LDS gathered in any orientation and
+// contracted as hi/lo bf16 (three MFMAs per step).  Used for fp32 inputs only,
+// where the bf16 tiling of the kernel above does not fit the LDS.
 // 8 values M[r][k..k+7] of a row-major fp32 matrix (contiguous).
 __device__ __forceinline__ void g8_row(float (&x)[8], const float* M, int ld, int r, int k) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)r * ld + k);
@@ -434,11 +1219,6 @@ __device__ __forceinline__ f32x4 gemm_blk(f32x4 acc, const float* A, int lda, co
     return acc;
 }
 
-__device__ __forceinline__ void st_blk(float* M, int ld, int m0, int n0, f32x4 x, int qg, int cl) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) M[(m0 + 4 * qg + i) * ld + n0 + cl] = x[i];
-}
-
 template <int DK, int DV>
 struct __attribute__((aligned(32))) ChunkSmem {
     static constexpr int LD = (DK > DV ? DK : DV) + 4;   // row stride of the 64 x d slots
@@ -456,20 +1236,8 @@ struct __attribute__((aligned(32))) ChunkSmem {
     float dbv[4][kChunk];  // per-wave row partials of sum_v v * dBV
 };
 
-// Find the sequence that owns state slot `slot` (slot = floor(cu[n]/64) + n + j).
-__device__ __forceinline__ int slot_owner(const int32_t* cu, int N, int seqlen, int64_t slot) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        const int64_t start = cu ? (int64_t)cu[mid] : (int64_t)mid * seqlen;
-        if (start / kChunk + mid <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 template <typename T, typename TO, int DK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParams p) {
     __shared__ ChunkSmem<DK, DV> sm;
     constexpr int LD = ChunkSmem<DK, DV>::LD;
     constexpr int LQ = ChunkSmem<DK, DV>::LQ;
@@ -1003,10 +1771,17 @@ template <typename T, typename TO, int DK>
 static hipError_t launch_chunk(const BwdParams& p, hipStream_t s) {
     const int64_t blocks = num_slots(p.T, p.N) * p.H;
     const dim3 grid((unsigned)blocks), block(kThreads);
-    if (p.dv == 128)
-        hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 128>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 64>), grid, block, 0, s, p);
+    if constexpr (std::is_same<T, float>::value) {
+        if (p.dv == 128)
+            hipLaunchKernelGGL((kda_bwd_chunk_f32_kernel<T, TO, DK, 128>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_bwd_chunk_f32_kernel<T, TO, DK, 64>), grid, block, 0, s, p);
+    } else {
+        if (p.dv == 128)
+            hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 128>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 64>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 
