@@ -214,6 +214,9 @@ template <int N> struct RawRow<bf16, N> {
     __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const u16n*>(p); }
     __device__ __forceinline__ void zero() { x = (u16n)0; }
     __device__ __forceinline__ float operator[](int j) const { return __uint_as_float(((unsigned)x[j]) << 16); }
+    // Hide the value from the optimiser so widened copies made before this
+    // point are not kept alive for uses after it.
+    __device__ __forceinline__ void fence() { asm volatile("" : "+v"(x)); }
 };
 template <int N> struct RawRow<float, N> {
     typedef float fn __attribute__((ext_vector_type(N)));
@@ -221,6 +224,7 @@ template <int N> struct RawRow<float, N> {
     __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const fn*>(p); }
     __device__ __forceinline__ void zero() { x = (fn)0.f; }
     __device__ __forceinline__ float operator[](int j) const { return x[j]; }
+    __device__ __forceinline__ void fence() { asm volatile("" : "+v"(x)); }
 };
 
 // One input scalar kept in storage format until used.

@@ -446,13 +446,446 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
     }
 }
 
+// ============================================================================
+// bf16 inputs: 8 waves in two groups of four.
+//
+// The state-coupled work of chunk n (U, O, the state update) runs on the four
+// "state" waves, which own the value columns as in the kernel above.  While
+// they run it, the four "prep" waves do all the per-element work of chunk n+1
+// in registers (norms, sigmoid, gate cumulative sum, exp2, the hi/lo operand
+// values) and issue the loads of chunk n+2.  The intra-chunk products, the
+// diagonal inverses and the blocked solve are shared by the two groups.  Each
+// SIMD carries one wave of each group, so the prep waves' VALU work fills the
+// state waves' MFMA and LDS latency.
+// ============================================================================
+constexpr int kFwdThreads = 512;
+
+template <typename TO, int DK, bool SAVE>
+__global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
+    typedef bf16 T;
+    __shared__ FwdSmem<T, DK> sm;
+    typedef FwdSmem<T, DK> SM;
+    constexpr int PK = SM::PK;
+    constexpr int PC = SM::PC;
+    constexpr int CPL = DK / 16;    // key columns per lane (prep layout)
+    constexpr int CQ = CPL / 4;     // 4-element groups per lane row
+    constexpr int VPL = kSlice / 16;
+    constexpr int NKB = DK / 32;    // k32 steps over dk
+    constexpr int NMB = DK / 16;    // 16-row blocks of the state
+    constexpr int NWB = DK / 64;    // W column blocks per prep wave in the solve
+    typedef bf16x8 V8T;
+    typedef bf16x4 V4T;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const bool is_state = w < 4;      // wave-uniform
+    const int ww = w & 3;             // index inside the group
+    int chain, slice;
+    map_block(blockIdx.x, p.N * p.H, p.nslices, chain, slice);
+    const int n = chain / p.H, h = chain % p.H;
+    int64_t t0, t1;
+    seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
+    const int dv = p.dv, H = p.H;
+    const int dv0 = slice * kSlice;
+    const int vcol = dv0 + 16 * ww + cl;   // value column of a state-wave lane
+
+    const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
+    const T* __restrict__ kp = reinterpret_cast<const T*>(p.k);
+    const T* __restrict__ vp = reinterpret_cast<const T*>(p.v);
+    const T* __restrict__ gp = reinterpret_cast<const T*>(p.g);
+    const T* __restrict__ bp = reinterpret_cast<const T*>(p.b);
+    TO* __restrict__ op = reinterpret_cast<TO*>(p.o);
+    const int64_t rs_k = (int64_t)H * DK, rs_v = (int64_t)H * dv;   // token strides
+
+    // ---------------- prep waves: rows 16ww+4qg+i, key columns CPL*cl+e
+    RawRow<T, CPL> rq[4], rk[4], rg[4];   // raw rows of the chunk being prepared
+    RawRow<T, VPL> rv[4];
+    RawScalar<T> rb[4];
+    float gx[CPL], nq[4], nk[4], beta[4];   // gx: in-wave exclusive gate prefix (log2 units)
+    int Lp = 0;                           // valid rows of the chunk being prepared
+    // prepared operand values of the next chunk to run (bf16 hi/lo, 4 columns per vector)
+    V4T xkil[4][CQ];                      // kh/Gam lo of the next chunk
+    float xgc[CPL];                       // Gam_C of the next chunk
+
+    auto load_chunk = [&](int64_t c0) {
+        const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+        const int r0 = 16 * ww + 4 * qg;
+        // uniform chunk bases (scalar registers) + 32-bit per-lane offsets
+        const T* qc = qp + c0 * rs_k + h * DK;
+        const T* kc = kp + c0 * rs_k + h * DK;
+        const T* gc = gp + c0 * rs_k + h * DK;
+        const T* vc = vp + c0 * rs_v + h * dv + dv0;
+        const T* bc = bp + c0 * H + h;
+        const int ok = r0 * (int)rs_k + CPL * cl, ov = r0 * (int)rs_v + VPL * cl, ob = r0 * H;
+        const int sk = (int)rs_k, sv = (int)rs_v;
+        if (r0 + 4 <= L) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                rq[i].load(qc + (ok + i * sk));
+                rk[i].load(kc + (ok + i * sk));
+                rg[i].load(gc + (ok + i * sk));
+                rv[i].load(vc + (ov + i * sv));
+                rb[i].load(bc + (ob + i * H));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (r0 + i < L) {
+                    rq[i].load(qc + (ok + i * sk));
+                    rk[i].load(kc + (ok + i * sk));
+                    rg[i].load(gc + (ok + i * sk));
+                    rv[i].load(vc + (ov + i * sv));
+                    rb[i].load(bc + (ob + i * H));
+                } else {
+                    rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
+                    rb[i].zero();
+                }
+            }
+        }
+        Lp = L;
+    };
+    // first half of the prep: norms, sigmoid, the in-wave part of the gate cumsum
+    auto prep_a = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); }
+            // reciprocal norms (v_rsq, ~1 ulp); the norms themselves are saved
+            nq[i] = __builtin_amdgcn_rsqf(sq + p.eps);
+            nk[i] = __builtin_amdgcn_rsqf(sk + p.eps);
+            const int r = 16 * ww + 4 * qg + i;
+            beta[i] = (r < Lp) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i].f())) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            float tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot += rg[i][e] * kLog2e;
+            float s = tot, x;
+            x = __shfl_up(s, 16);
+            if (qg >= 1) s += x;
+            x = __shfl_up(s, 32);
+            if (qg >= 2) s += x;
+            gx[e] = s - tot;
+            if (qg == 3) sm.red[ww][CPL * cl + e] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { rq[i].fence(); rk[i].fence(); rg[i].fence(); }
+    };
+    // second half (after the prep waves' column sums are in LDS): finish G and
+    // form the operand values.  kh/Gam lo and Gam_C stay in registers until the
+    // chunk's first step (the state waves still read those tiles while this
+    // runs); every other tile is written now.
+    auto prep_b = [&](int64_t c0) {
+        float run[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int c = CPL * cl + e;
+            float a = 0.f, tot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const float x = sm.red[w2][c];
+                if (w2 < ww) a += x;
+                tot += x;
+            }
+            run[e] = gx[e] + a;
+            xgc[e] = fast_exp2(tot);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ww + 4 * qg + i;
+            const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
+#pragma unroll
+            for (int e4 = 0; e4 < CQ; ++e4) {
+                f32x4 vq, vk, vi;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * e4 + j;
+                    run[e] += rg[i][e] * kLog2e;
+                    const float gam = fast_exp2(run[e]);
+                    const float gin = fast_exp2(-run[e]);
+                    vq[j] = (rq[i][e] * aq) * gam;
+                    vk[j] = (rk[i][e] * ak) * gam;
+                    vi[j] = (rk[i][e] * ai) * gin;
+                }
+                const int pc = perm32(CPL * cl + 4 * e4);
+                sts4_split<T, true>(&sm.qg[r * PK + pc], &sm.qgl[r * PK + pc], vq);
+                const V4T kih = pack4<T>(vi);
+                xkil[i][e4] = pack4<T>(vi - unpack4(kih));
+                *reinterpret_cast<V4T*>(&sm.kg[r * PK + pc]) = pack4<T>(vk);
+                *reinterpret_cast<V4T*>(&sm.ki[r * PK + pc]) = kih;
+            }
+            if (cl == 0) sm.beta[r] = beta[i];
+            if (SAVE && slice == 0 && cl == 0 && r < Lp) {
+                p.nq_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nq[i]);
+                p.nk_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nk[i]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) {
+            f32x4 x = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
+            sts4<T>(&sm.vt[(VPL * cl + e) * PC + 16 * ww + 4 * qg], x);   // exact: v is an input value
+        }
+    };
+
+    // The k32 steps of Aqk U read the upper 16x16 blocks (0,1) and (2,3) of the
+    // Aqk tiles, which no chunk writes: clear them once.  (The first barrier
+    // inside the chunk loop orders this before any read.)
+    for (int e = tid; e < kChunk * PC; e += kFwdThreads) {
+        sm.aqk[e] = from_f32<T>(0.f);
+        sm.aqkl[e] = from_f32<T>(0.f);
+    }
+
+    // step 2, shared by both groups: Akk and Aqk, one lower-triangle block pair per item
+    auto intra_products = [&]() {
+#pragma unroll 1
+        for (int it = w; it < 10; it += 8) {
+            const int ib = it >= 6 ? 3 : (it >= 3 ? 2 : (it >= 1 ? 1 : 0));
+            const int jb = it - (ib * (ib + 1)) / 2;
+            const int ra = (16 * ib + cl) * PK + 8 * qg, rbk = (16 * jb + cl) * PK + 8 * qg;
+            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKB; ++kk) {
+                const V8T bh = lds8<T>(sm.ki + rbk + 32 * kk);
+                akk = mma_k32(akk, lds8<T>(sm.kg + ra + 32 * kk), bh);
+                aqk = mma3<true>(aqk, lds8<T>(sm.qg + ra + 32 * kk), lds8<T>(sm.qgl + ra + 32 * kk), bh,
+                                 lds8<T>(sm.kil + rbk + 32 * kk));
+            }
+            const int s = 16 * jb + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ib + 4 * qg + i;
+                const float vq = s <= r ? aqk[i] : 0.f;
+                const T hi = from_f32<T>(vq);
+                sm.aqk[r * PC + perm32(s)] = hi;
+                sm.aqkl[r * PC + perm32(s)] = from_f32<T>(vq - to_f32(hi));
+                const float vk = s < r ? akk[i] : 0.f;
+                sm.akk[r * PC + s] = from_f32<T>(vk);
+                if (ib == jb) sm.adiag[ib][4 * qg + i][cl] = vk;
+            }
+        }
+    };
+    // diagonal inverses of I + Akk as bf16 k16 A fragments
+    auto load_tii = [&](V4T (&tii)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tii[i] = pack4<T>(*reinterpret_cast<const f32x4*>(&sm.tdiag[i][cl][4 * qg]));
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // The two groups run separate loops with the same barrier sequence: one
+    // barrier after the prologue, then six per chunk.
+    if (is_state) {
+        // ---------------------------------------------------------------- state waves
+        const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
+        f32x4 S[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
+        if (t0 < t1) __syncthreads();   // prologue (prep waves: first chunk's operand values)
+        int64_t slot = t0 / kChunk + n;
+        for (int64_t c0 = t0; c0 < t1; c0 += kChunk, ++slot) {
+            const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+            // 1: save the entering state of this chunk (fp32)
+            if (SAVE) {
+                float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+            }
+            __syncthreads();
+            // 2
+            intra_products();
+            __syncthreads();
+            // 3: (I + Akk_bb)^{-1}, block b = this wave
+            {
+                const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
+                f32x4 nb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) nb[j] = sm.adiag[ww][4 * qg + j][cl];
+                const f32x4 tw = inv_unit_lower16(na, nb, qg, cl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
+            }
+            __syncthreads();
+            // 4: Ut = (I + Akk)^{-1} diag(beta) v for this wave's 16 value columns
+            f32x4 Ut[4];
+            {
+                V4T tii[4];
+                load_tii(tii);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 vv = lds4f<T>(&sm.vt[(16 * ww + cl) * PC + 16 * i + 4 * qg]);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(&sm.beta[16 * i + 4 * qg]);
+                    f32x4 acc = vv * bb;   // beta v, exact in fp32
+#pragma unroll
+                    for (int jp = 0; jp < i; ++jp)
+                        acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])), pack4<T>(Ut[jp]));
+                    const V4T ah = pack4<T>(acc);
+                    Ut[i] = mma_k16(zero, tii[i], ah);
+                    Ut[i] = mma_k16(Ut[i], tii[i], pack4<T>(acc - unpack4(ah)));
+                }
+            }
+            __syncthreads();
+            // 5a: U = Ut - W S  (the tile holds -W) ;  O = (qh Gam) S
+            f32x4 O[4];
+            V8T ufh[2], ufl[2];
+            {
+                V8T sfh[NKB], sfl[NKB];
+#pragma unroll
+                for (int kk = 0; kk < NKB; ++kk) split8<T, true>(S[2 * kk], S[2 * kk + 1], sfh[kk], sfl[kk]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ro = (16 * i + cl) * PK + 8 * qg;
+                    O[i] = zero;
+#pragma unroll
+                    for (int kk = 0; kk < NKB; ++kk) {
+                        Ut[i] = mma_k32(Ut[i], lds8<T>(sm.ki + ro + 32 * kk), sfh[kk]);
+                        O[i] = mma3<true>(O[i], lds8<T>(sm.qg + ro + 32 * kk), lds8<T>(sm.qgl + ro + 32 * kk), sfh[kk],
+                                          sfl[kk]);
+                    }
+                }
+            }
+            split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
+            split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
+            __syncthreads();
+            // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ra = (16 * i + cl) * PC + 8 * qg;
+#pragma unroll
+                for (int kk = 0; kk <= (i >> 1); ++kk)
+                    O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + ra + 32 * kk), lds8<T>(sm.aqkl + ra + 32 * kk), ufh[kk],
+                                      ufl[kk]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * i + 4 * qg + j;
+                    if (r < L) op[((c0 + r) * H + h) * dv + vcol] = from_f32<TO>(O[i][j]);
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
+                S[mb] *= gcv;
+                const int rt = (16 * mb + cl) * PC + 8 * qg;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    S[mb] = mma3<true>(S[mb], lds8<T>(sm.kt + rt + 32 * kk), lds8<T>(sm.kil + rt + 32 * kk), ufh[kk],
+                                       ufl[kk]);
+            }
+            __syncthreads();
+        }
+        if (p.sfinal) {
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p.sfinal[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+        }
+    } else {
+        // ---------------------------------------------------------------- prep waves
+        if (t0 < t1) {
+            load_chunk(t0);
+            prep_a();
+            __syncthreads();
+            prep_b(t0);
+            if (t0 + kChunk < t1) load_chunk(t0 + kChunk);
+        }
+        for (int64_t c0 = t0; c0 < t1; c0 += kChunk) {
+            const bool more = c0 + kChunk < t1;
+            // 1: the remaining operand tiles of this chunk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ww + 4 * qg + i;
+#pragma unroll
+                for (int e4 = 0; e4 < CQ; ++e4)
+                    *reinterpret_cast<V4T*>(&sm.kil[r * PK + perm32(CPL * cl + 4 * e4)]) = xkil[i][e4];
+            }
+            if (ww == 0 && qg == 0) {
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
+            }
+            __syncthreads();
+            // 2
+            intra_products();
+            __syncthreads();
+            // 3: Ktil^T = (kh Gam_C / Gam)^T from the kh/Gam hi+lo values; its lo
+            // tile goes where kh/Gam lo lived (read only by step 2)
+            {
+                const int pr = perm32(16 * ww + 4 * qg);
+#pragma unroll
+                for (int e4 = 0; e4 < CQ; ++e4) {
+                    f32x4 kv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        kv[i] = lds4f<T>(&sm.ki[(16 * ww + 4 * qg + i) * PK + perm32(CPL * cl + 4 * e4)]) +
+                                unpack4(xkil[i][e4]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = 4 * e4 + j;
+                        f32x4 x = {kv[0][j] * xgc[e], kv[1][j] * xgc[e], kv[2][j] * xgc[e], kv[3][j] * xgc[e]};
+                        sts4_split<T, true>(&sm.kt[(CPL * cl + e) * PC + pr], &sm.kil[(CPL * cl + e) * PC + pr], x);
+                    }
+                }
+            }
+            __syncthreads();
+            // 4: W = (I + Akk)^{-1} beta kh Gam for key column blocks ww + 4cb, stored
+            // negated over the kh/Gam hi tile
+            {
+                V4T tii[4];
+                load_tii(tii);
+#pragma unroll
+                for (int cb = 0; cb < NWB; ++cb) {
+                    const int pc = perm32(16 * (ww + 4 * cb) + cl);
+                    f32x4 X[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        f32x4 acc;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[j] = to_f32(sm.kg[(16 * i + 4 * qg + j) * PK + pc]);
+#pragma unroll
+                        for (int jp = 0; jp < i; ++jp)
+                            acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])),
+                                          pack4<T>(X[jp]));
+                        X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sm.ki[(16 * i + 4 * qg + j) * PK + pc] = from_f32<T>(-X[i][j]);
+                }
+            }
+            __syncthreads();
+            // 5a: norms, sigmoid and in-wave gate sums of the next chunk
+            if (more) prep_a();
+            __syncthreads();
+            // 5b: operand values of the next chunk; loads of the one after
+            if (more) {
+                prep_b(c0 + kChunk);
+                if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);
+            }
+            __syncthreads();
+        }
+    }
+}
+
 template <typename T, typename TO, int DK>
 static hipError_t launch_fwd_t(const FwdParams& p, bool save, hipStream_t s) {
-    const dim3 grid((unsigned)(p.N * p.H * p.nslices)), block(kThreads);
-    if (save)
-        hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, false>), grid, block, 0, s, p);
+    const dim3 grid((unsigned)(p.N * p.H * p.nslices));
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (save)
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, true>), grid, dim3(kFwdThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, false>), grid, dim3(kFwdThreads), 0, s, p);
+    } else {
+        if (save)
+            hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, true>), grid, dim3(kThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, false>), grid, dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 
