@@ -69,10 +69,8 @@ __device__ __forceinline__ f32x4 mma_k16(f32x4 c, f32x4 a, f32x4 b) {
 // ------------------------------------------------------------ fragments
 template <typename T> __device__ __forceinline__ typename V8<T>::t pack8(f32x4 lo, f32x4 hi);
 template <> __device__ __forceinline__ bf16x8 pack8<bf16>(f32x4 lo, f32x4 hi) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { r[j] = (bf16)lo[j]; r[j + 4] = (bf16)hi[j]; }
-    return r;
+    const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 template <> __device__ __forceinline__ f32x8 pack8<float>(f32x4 lo, f32x4 hi) {
     f32x8 r;
@@ -81,12 +79,7 @@ template <> __device__ __forceinline__ f32x8 pack8<float>(f32x4 lo, f32x4 hi) {
     return r;
 }
 template <typename T> __device__ __forceinline__ typename V4<T>::t pack4(f32x4 x);
-template <> __device__ __forceinline__ bf16x4 pack4<bf16>(f32x4 x) {
-    bf16x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
-    return r;
-}
+template <> __device__ __forceinline__ bf16x4 pack4<bf16>(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 template <> __device__ __forceinline__ f32x4 pack4<float>(f32x4 x) { return x; }
 
 
@@ -147,6 +140,26 @@ template <typename T> __device__ __forceinline__ f32x4 lds4f(const T* p) {
 __device__ __forceinline__ int perm32(int k) {
     const int kk = k & 31;
     return (k & ~31) | (((kk >> 2) & 3) << 3) | ((kk >> 4) << 2) | (kk & 3);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
+// release/acquire fence as well, which waits for every outstanding global load
+// of the wave (vmcnt(0)) and so drains register prefetches at each barrier;
+// this one waits for the wave's LDS operations and meets the other waves.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Sum over the 16 lanes of a DPP row (lanes 16q..16q+15), returned to every
+// lane of the row; the butterfly order makes all 16 results bitwise equal.
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    return v;
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }

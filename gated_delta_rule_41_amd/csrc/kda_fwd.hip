@@ -460,6 +460,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 // ============================================================================
 constexpr int kFwdThreads = 512;
 
+// Ktil^T tile of the bf16 kernel: rows c (key channel), 64 positions (chunk row
+// index r, permuted by perm32) per row, no padding; the 16-byte group of a
+// position is XOR-swizzled with (c ^ c>>3) & 7.  The A-fragment reads (16
+// consecutive rows) and the prep waves' writes (rows 8 apart) then spread over
+// the LDS banks.
+__device__ __forceinline__ int kt_off(int c, int pos) {
+    return c * kChunk + ((((pos >> 3) ^ (c ^ (c >> 3))) & 7) << 3) + (pos & 7);
+}
+
 template <typename TO, int DK, bool SAVE>
 __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
     typedef bf16 T;
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
     RawRow<T, CPL> rq[4], rk[4], rg[4];   // raw rows of the chunk being prepared
     RawRow<T, VPL> rv[4];
     RawScalar<T> rb[4];
-    float gx[CPL], nq[4], nk[4], beta[4];   // gx: in-wave exclusive gate prefix (log2 units)
+    float nq[4], nk[4], beta[4];
     int Lp = 0;                           // valid rows of the chunk being prepared
     // prepared operand values of the next chunk to run (bf16 hi/lo, 4 columns per vector)
     V4T xkil[4][CQ];                      // kh/Gam lo of the next chunk
@@ -543,15 +552,27 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
         }
         Lp = L;
     };
-    // first half of the prep: norms, sigmoid, the in-wave part of the gate cumsum
+    // In-wave inclusive prefix of the gates over the wave's 16 rows, for key
+    // column CPL*cl+e: one k16 MFMA of the lower-triangular ones matrix with the
+    // raw bf16 gates, which already sit in B-fragment layout (lane (qg, cl)
+    // holds rows 4qg..4qg+3 of the column).  Exact products, fp32 sums; the
+    // result comes back in the same rows.
+    V4T ltri;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
+    auto gate_prefix = [&](int e) {
+        const V4T b = __builtin_bit_cast(V4T, u16x4{rg[0].x[e], rg[1].x[e], rg[2].x[e], rg[3].x[e]});
+        return mma_k16(f32x4{0.f, 0.f, 0.f, 0.f}, ltri, b);
+    };
+    // first half of the prep: norms, sigmoid, the wave's gate column sums
     auto prep_a = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); }
+            sq = row16_sum(sq);
+            sk = row16_sum(sk);
             // reciprocal norms (v_rsq, ~1 ulp); the norms themselves are saved
             nq[i] = __builtin_amdgcn_rsqf(sq + p.eps);
             nk[i] = __builtin_amdgcn_rsqf(sk + p.eps);
@@ -560,16 +581,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            float tot = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tot += rg[i][e] * kLog2e;
-            float s = tot, x;
-            x = __shfl_up(s, 16);
-            if (qg >= 1) s += x;
-            x = __shfl_up(s, 32);
-            if (qg >= 2) s += x;
-            gx[e] = s - tot;
-            if (qg == 3) sm.red[ww][CPL * cl + e] = s;
+            const f32x4 gp = gate_prefix(e);
+            if (qg == 3) sm.red[ww][CPL * cl + e] = gp[3];   // row 15: the wave's column sum
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { rq[i].fence(); rk[i].fence(); rg[i].fence(); }
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
     // chunk's first step (the state waves still read those tiles while this
     // runs); every other tile is written now.
     auto prep_b = [&](int64_t c0) {
-        float run[CPL];
+        float goff[CPL];   // other prep waves' rows above this wave (raw gate units)
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
             const int c = CPL * cl + e;
@@ -590,33 +603,43 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
                 if (w2 < ww) a += x;
                 tot += x;
             }
-            run[e] = gx[e] + a;
-            xgc[e] = fast_exp2(tot);
+            goff[e] = a;
+            xgc[e] = fast_exp2(tot * kLog2e);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ww + 4 * qg + i;
-            const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
+        for (int e4 = 0; e4 < CQ; ++e4) {
+            f32x4 G[4];   // G[j][i]: gate cumsum (log2 units) at row 16ww+4qg+i, column CPL*cl+4e4+j
 #pragma unroll
-            for (int e4 = 0; e4 < CQ; ++e4) {
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 gp = gate_prefix(4 * e4 + j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) G[j][i] = (gp[i] + goff[4 * e4 + j]) * kLog2e;
+            }
+            const int pc = perm32(CPL * cl + 4 * e4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ww + 4 * qg + i;
+                const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
                 f32x4 vq, vk, vi;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int e = 4 * e4 + j;
-                    run[e] += rg[i][e] * kLog2e;
-                    const float gam = fast_exp2(run[e]);
-                    const float gin = fast_exp2(-run[e]);
+                    const float gam = fast_exp2(G[j][i]);
+                    const float gin = fast_exp2(-G[j][i]);
                     vq[j] = (rq[i][e] * aq) * gam;
                     vk[j] = (rk[i][e] * ak) * gam;
                     vi[j] = (rk[i][e] * ai) * gin;
                 }
-                const int pc = perm32(CPL * cl + 4 * e4);
                 sts4_split<T, true>(&sm.qg[r * PK + pc], &sm.qgl[r * PK + pc], vq);
                 const V4T kih = pack4<T>(vi);
                 xkil[i][e4] = pack4<T>(vi - unpack4(kih));
                 *reinterpret_cast<V4T*>(&sm.kg[r * PK + pc]) = pack4<T>(vk);
                 *reinterpret_cast<V4T*>(&sm.ki[r * PK + pc]) = kih;
             }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ww + 4 * qg + i;
             if (cl == 0) sm.beta[r] = beta[i];
             if (SAVE && slice == 0 && cl == 0 && r < Lp) {
                 p.nq_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nq[i]);
@@ -685,7 +708,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
-        if (t0 < t1) __syncthreads();   // prologue (prep waves: first chunk's operand values)
+        if (t0 < t1) lds_barrier();   // prologue (prep waves: first chunk's operand values)
         int64_t slot = t0 / kChunk + n;
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk, ++slot) {
             const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
@@ -697,10 +720,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
             }
-            __syncthreads();
+            lds_barrier();
             // 2
             intra_products();
-            __syncthreads();
+            lds_barrier();
             // 3: (I + Akk_bb)^{-1}, block b = this wave
             {
                 const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
@@ -711,7 +734,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
             }
-            __syncthreads();
+            lds_barrier();
             // 4: Ut = (I + Akk)^{-1} diag(beta) v for this wave's 16 value columns
             f32x4 Ut[4];
             {
@@ -730,7 +753,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
                     Ut[i] = mma_k16(Ut[i], tii[i], pack4<T>(acc - unpack4(ah)));
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // 5a: U = Ut - W S  (the tile holds -W) ;  O = (qh Gam) S
             f32x4 O[4];
             V8T ufh[2], ufl[2];
@@ -752,7 +775,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
             }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
-            __syncthreads();
+            lds_barrier();
             // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -771,13 +794,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
             for (int mb = 0; mb < NMB; ++mb) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
                 S[mb] *= gcv;
-                const int rt = (16 * mb + cl) * PC + 8 * qg;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    S[mb] = mma3<true>(S[mb], lds8<T>(sm.kt + rt + 32 * kk), lds8<T>(sm.kil + rt + 32 * kk), ufh[kk],
-                                       ufl[kk]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int rt = kt_off(16 * mb + cl, 32 * kk + 8 * qg);
+                    S[mb] = mma3<true>(S[mb], lds8<T>(sm.kt + rt), lds8<T>(sm.kil + rt), ufh[kk], ufl[kk]);
+                }
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (p.sfinal) {
 #pragma unroll
@@ -790,7 +813,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
         if (t0 < t1) {
             load_chunk(t0);
             prep_a();
-            __syncthreads();
+            lds_barrier();
             prep_b(t0);
             if (t0 + kChunk < t1) load_chunk(t0 + kChunk);
         }
@@ -808,10 +831,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
 #pragma unroll
                 for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
             }
-            __syncthreads();
+            lds_barrier();
             // 2
             intra_products();
-            __syncthreads();
+            lds_barrier();
             // 3: Ktil^T = (kh Gam_C / Gam)^T from the kh/Gam hi+lo values; its lo
             // tile goes where kh/Gam lo lived (read only by step 2)
             {
@@ -827,11 +850,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
                     for (int j = 0; j < 4; ++j) {
                         const int e = 4 * e4 + j;
                         f32x4 x = {kv[0][j] * xgc[e], kv[1][j] * xgc[e], kv[2][j] * xgc[e], kv[3][j] * xgc[e]};
-                        sts4_split<T, true>(&sm.kt[(CPL * cl + e) * PC + pr], &sm.kil[(CPL * cl + e) * PC + pr], x);
+                        sts4_split<T, true>(&sm.kt[kt_off(CPL * cl + e, pr)], &sm.kil[kt_off(CPL * cl + e, pr)], x);
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // 4: W = (I + Akk)^{-1} beta kh Gam for key column blocks ww + 4cb, stored
             // negated over the kh/Gam hi tile
             {
@@ -858,16 +881,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
                         for (int j = 0; j < 4; ++j) sm.ki[(16 * i + 4 * qg + j) * PK + pc] = from_f32<T>(-X[i][j]);
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // 5a: norms, sigmoid and in-wave gate sums of the next chunk
             if (more) prep_a();
-            __syncthreads();
+            lds_barrier();
             // 5b: operand values of the next chunk; loads of the one after
             if (more) {
                 prep_b(c0 + kChunk);
                 if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
