@@ -382,6 +382,391 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_scan_kernel(BwdParams p) 
 }
 
 // ============================================================================
+// B1 for bf16 inputs: 8 waves in two groups of four, as in the forward.
+// The state waves own the dL/dS columns (diagonal inverses, dU and the dS
+// step); the prep waves prepare the previous chunk in registers while the
+// state waves run the step, and prefetch the one before it.
+// ============================================================================
+template <int DK>
+__global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdParams p) {
+    typedef bf16 T;
+    __shared__ ScanSmem<T, DK> sm;
+    typedef ScanSmem<T, DK> SM;
+    constexpr int PK = SM::PK;
+    constexpr int PC = SM::PC;
+    constexpr int CPL = DK / 16;
+    constexpr int CQ = CPL / 4;
+    constexpr int VPL = kSlice / 16;
+    constexpr int NKB = DK / 32;
+    constexpr int NMB = DK / 16;
+    typedef bf16x8 V8T;
+    typedef bf16x4 V4T;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const bool is_state = w < 4;
+    const int ww = w & 3;
+    int chain, slice;
+    map_block(blockIdx.x, p.N * p.H, p.nslices, chain, slice);
+    const int n = chain / p.H, h = chain % p.H;
+    int64_t t0, t1;
+    seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
+    const int dv = p.dv, H = p.H;
+    const int dv0 = slice * kSlice;
+    const int vcol = dv0 + 16 * ww + cl;
+    const int64_t nchunks = (t1 - t0 + kChunk - 1) / kChunk;
+
+    const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
+    const T* __restrict__ kp = reinterpret_cast<const T*>(p.k);
+    const T* __restrict__ gp = reinterpret_cast<const T*>(p.g);
+    const T* __restrict__ bp = reinterpret_cast<const T*>(p.b);
+    const T* __restrict__ dop = reinterpret_cast<const T*>(p.dO);
+    const int64_t rs_k = (int64_t)H * DK, rs_v = (int64_t)H * dv;
+
+    // ---------------- prep waves: rows 16ww+4qg+i, key columns CPL*cl+e
+    RawRow<T, CPL> rq[4], rk[4], rg[4];
+    RawRow<T, VPL> rdo[4];
+    RawScalar<T> rb[4];
+    float nq[4], nk[4], beta[4];
+    int Lp = 0;
+    V4T xqh[4][CQ], xql[4][CQ];   // qh Gam hi/lo of the chunk to run next
+    RawRow<T, VPL> xdo[4];        // its dO slice
+    float xgc[CPL];               // its Gam_C
+
+    auto load_chunk = [&](int64_t c0) {
+        const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+        const int r0 = 16 * ww + 4 * qg;
+        const T* qc = qp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* kc = kp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* gc = gp + (c0 + r0) * rs_k + h * DK + CPL * cl;
+        const T* dc = dop + (c0 + r0) * rs_v + h * dv + dv0 + VPL * cl;
+        const T* bc = bp + (c0 + r0) * H + h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (r0 + i < L) {
+                rq[i].load(qc + i * rs_k);
+                rk[i].load(kc + i * rs_k);
+                rg[i].load(gc + i * rs_k);
+                rdo[i].load(dc + i * rs_v);
+                rb[i].load(bc + i * H);
+            } else {
+                rq[i].zero(); rk[i].zero(); rg[i].zero(); rdo[i].zero();
+                rb[i].zero();
+            }
+        }
+        Lp = L;
+    };
+    V4T ltri;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
+    auto gate_prefix = [&](int e) {
+        const V4T b = __builtin_bit_cast(V4T, u16x4{rg[0].x[e], rg[1].x[e], rg[2].x[e], rg[3].x[e]});
+        return mma_k16(f32x4{0.f, 0.f, 0.f, 0.f}, ltri, b);
+    };
+    auto prep_a = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
+            sq = row16_sum(sq);
+            sk = row16_sum(sk);
+            nq[i] = __builtin_amdgcn_rsqf(sq + p.eps);   // reciprocal norms
+            nk[i] = __builtin_amdgcn_rsqf(sk + p.eps);
+            const int r = 16 * ww + 4 * qg + i;
+            beta[i] = (r < Lp) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i].f())) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const f32x4 gp4 = gate_prefix(e);
+            if (qg == 3) sm.red[ww][CPL * cl + e] = gp4[3];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { rq[i].fence(); rk[i].fence(); rg[i].fence(); }
+    };
+    // qh Gam (hi, lo), its dO slice and Gam_C stay in registers (the state
+    // waves still read those tiles while this runs); beta kh Gam and kh/Gam
+    // (hi, lo) are written now.
+    auto prep_b = [&]() {
+        float goff[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int c = CPL * cl + e;
+            float a = 0.f, tot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const float x = sm.red[w2][c];
+                if (w2 < ww) a += x;
+                tot += x;
+            }
+            goff[e] = a;
+            xgc[e] = fast_exp2(tot * kLog2e);
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < CQ; ++e4) {
+            f32x4 G[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 gp4 = gate_prefix(4 * e4 + j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) G[j][i] = (gp4[i] + goff[4 * e4 + j]) * kLog2e;
+            }
+            const int pc = perm32(CPL * cl + 4 * e4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ww + 4 * qg + i;
+                const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
+                f32x4 vq, vk, vi;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * e4 + j;
+                    const float gam = fast_exp2(G[j][i]);
+                    const float gin = fast_exp2(-G[j][i]);
+                    vq[j] = (rq[i][e] * aq) * gam;
+                    vk[j] = (rk[i][e] * ak) * gam;
+                    vi[j] = (rk[i][e] * ai) * gin;
+                }
+                xqh[i][e4] = pack4<T>(vq);
+                xql[i][e4] = pack4<T>(vq - unpack4(xqh[i][e4]));
+                *reinterpret_cast<V4T*>(&sm.kg[r * PK + pc]) = pack4<T>(vk);
+                sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], vi);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xdo[i] = rdo[i];
+    };
+
+    for (int e = tid; e < kChunk * PC; e += kWideThreads) {
+        sm.aqt[e] = from_f32<T>(0.f);    // Aqk^T blocks above the diagonal are never written
+        sm.aqtl[e] = from_f32<T>(0.f);
+    }
+    // step 2, shared: Akk and Aqk^T, one lower-triangle block pair per item
+    auto intra_products = [&]() {
+#pragma unroll 1
+        for (int it = w; it < 10; it += 8) {
+            const int ib = it >= 6 ? 3 : (it >= 3 ? 2 : (it >= 1 ? 1 : 0));
+            const int jb = it - (ib * (ib + 1)) / 2;
+            const int ra = (16 * ib + cl) * PK + 8 * qg, rbk = (16 * jb + cl) * PK + 8 * qg;
+            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKB; ++kk) {
+                const V8T bh = lds8<T>(sm.r2 + rbk + 32 * kk);
+                akk = mma_k32(akk, lds8<T>(sm.kg + ra + 32 * kk), bh);
+                aqk = mma3<true>(aqk, lds8<T>(sm.r0 + ra + 32 * kk), lds8<T>(sm.r1 + ra + 32 * kk), bh,
+                                 lds8<T>(sm.r3 + rbk + 32 * kk));
+            }
+            const int s = 16 * jb + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ib + 4 * qg + i;
+                const float vq = s <= r ? aqk[i] : 0.f;
+                const T hi = from_f32<T>(vq);
+                sm.aqt[s * PC + perm32(r)] = hi;
+                sm.aqtl[s * PC + perm32(r)] = from_f32<T>(vq - to_f32(hi));
+                const float vk = s < r ? akk[i] : 0.f;
+                sm.akk[r * PC + s] = from_f32<T>(vk);
+                if (ib == jb) sm.adiag[ib][4 * qg + i][cl] = vk;
+            }
+        }
+    };
+    // step 4, shared: W = (I + Akk)^{-1} beta kh Gam for key column block w; store -W^T
+    auto w_solve = [&]() {
+        if (w < DK / 16) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            V4T tii[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tii[i] = pack4<T>(*reinterpret_cast<const f32x4*>(&sm.tdiag[i][cl][4 * qg]));
+            const int nb = 16 * w;
+            const int pc = perm32(nb + cl);
+            f32x4 X[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = to_f32(sm.kg[(16 * i + 4 * qg + j) * PK + pc]);
+#pragma unroll
+                for (int jp = 0; jp < i; ++jp)
+                    acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])), pack4<T>(X[jp]));
+                X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sts4<T>(&sm.wt[(nb + cl) * PC + perm32(16 * i + 4 * qg)], -X[i]);
+        }
+    };
+
+    if (is_state) {
+        // ---------------------------------------------------------------- state waves
+        float* __restrict__ dst = reinterpret_cast<float*>(p.dst_saved);
+        const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
+        f32x4 dS[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dS[mb][i] = p.dS_final ? p.dS_final[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
+        if (nchunks > 0) lds_barrier();   // prologue
+        for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
+            const int64_t slot = t0 / kChunk + n + jc;
+            // 1: dL/dS at the end of this chunk, for the chunk-parallel gradients
+            {
+                float* out = dst + (slot * H + h) * (int64_t)DK * dv;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) out[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
+            }
+            lds_barrier();
+            intra_products();
+            lds_barrier();
+            // 3: (I + Akk_bb)^{-1}, block b = this wave
+            {
+                const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
+                f32x4 nbv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) nbv[j] = sm.adiag[ww][4 * qg + j][cl];
+                const f32x4 tw = inv_unit_lower16(na, nbv, qg, cl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
+            }
+            lds_barrier();
+            w_solve();
+            lds_barrier();
+            // 5a: dU = Aqk^T dO + Ktil dS1
+            V8T dof[2], duf[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + (16 * ww + cl) * PC + 32 * kk + 8 * qg);
+            {
+                V8T dsh[NKB], dsl[NKB];
+#pragma unroll
+                for (int kk = 0; kk < NKB; ++kk) split8<T, true>(dS[2 * kk], dS[2 * kk + 1], dsh[kk], dsl[kk]);
+                f32x4 dU[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const int ra = (16 * i + cl) * PC + 8 * qg;
+#pragma unroll
+                    for (int kk = (i >> 1); kk < 2; ++kk) {
+                        acc = mma_k32(acc, lds8<T>(sm.aqt + ra + 32 * kk), dof[kk]);
+                        acc = mma_k32(acc, lds8<T>(sm.aqtl + ra + 32 * kk), dof[kk]);
+                    }
+                    const int rk2 = (16 * i + cl) * PK + 8 * qg;
+#pragma unroll
+                    for (int kk = 0; kk < NKB; ++kk)
+                        acc = mma3<true>(acc, lds8<T>(sm.r2 + rk2 + 32 * kk), lds8<T>(sm.r3 + rk2 + 32 * kk), dsh[kk],
+                                         dsl[kk]);
+                    dU[i] = acc;
+                }
+                duf[0] = pack8<T>(dU[0], dU[1]);
+                duf[1] = pack8<T>(dU[2], dU[3]);
+            }
+            lds_barrier();
+            // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
+                f32x4 acc = dS[mb] * gcv;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int rt = kt_off(16 * mb + cl, 32 * kk + 8 * qg);
+                    acc = mma_k32(acc, lds8<T>(sm.r0 + rt), dof[kk]);
+                    acc = mma_k32(acc, lds8<T>(sm.r1 + rt), dof[kk]);
+                    acc = mma_k32(acc, lds8<T>(sm.wt + (16 * mb + cl) * PC + 32 * kk + 8 * qg), duf[kk]);
+                }
+                dS[mb] = acc;
+            }
+            lds_barrier();
+        }
+        if (p.dS0) {
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p.dS0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
+        }
+    } else {
+        // ---------------------------------------------------------------- prep waves
+        if (nchunks > 0) {
+            const int64_t cl0 = t0 + (nchunks - 1) * kChunk;
+            load_chunk(cl0);
+            prep_a();
+            lds_barrier();
+            prep_b();
+            if (nchunks > 1) load_chunk(cl0 - kChunk);
+        }
+        for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
+            const int64_t c0 = t0 + jc * kChunk;
+            // 1: the tiles held in registers
+            {
+                const int pr = perm32(16 * ww + 4 * qg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * ww + 4 * qg + i;
+#pragma unroll
+                    for (int e4 = 0; e4 < CQ; ++e4) {
+                        const int pc = perm32(CPL * cl + 4 * e4);
+                        *reinterpret_cast<V4T*>(&sm.r0[r * PK + pc]) = xqh[i][e4];
+                        *reinterpret_cast<V4T*>(&sm.r1[r * PK + pc]) = xql[i][e4];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < VPL; ++e) {
+                    f32x4 x = {xdo[0][e], xdo[1][e], xdo[2][e], xdo[3][e]};
+                    sts4<T>(&sm.dot[(VPL * cl + e) * PC + pr], x);   // exact: dO is an input value
+                }
+                if (ww == 0 && qg == 0) {
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
+                }
+            }
+            lds_barrier();
+            intra_products();
+            lds_barrier();
+            // 3: (qh Gam)^T hi/lo over the qh Gam tiles (swizzled layout); Ktil = (kh/Gam) Gam_C
+            // in place of kh/Gam (each lane rewrites its own elements)
+            {
+                const int pr = perm32(16 * ww + 4 * qg);
+#pragma unroll
+                for (int e4 = 0; e4 < CQ; ++e4) {
+                    f32x4 hv[4], lv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { hv[i] = unpack4(xqh[i][e4]); lv[i] = unpack4(xql[i][e4]); }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = CPL * cl + 4 * e4 + j;
+                        *reinterpret_cast<V4T*>(&sm.r0[kt_off(c, pr)]) =
+                            pack4<T>(f32x4{hv[0][j], hv[1][j], hv[2][j], hv[3][j]});
+                        *reinterpret_cast<V4T*>(&sm.r1[kt_off(c, pr)]) =
+                            pack4<T>(f32x4{lv[0][j], lv[1][j], lv[2][j], lv[3][j]});
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * ww + 4 * qg + i;
+#pragma unroll
+                    for (int e4 = 0; e4 < CQ; ++e4) {
+                        const int pc = perm32(CPL * cl + 4 * e4);
+                        f32x4 x = lds4f<T>(&sm.r2[r * PK + pc]) + lds4f<T>(&sm.r3[r * PK + pc]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x[j] *= xgc[4 * e4 + j];
+                        sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], x);
+                    }
+                }
+            }
+            lds_barrier();
+            w_solve();
+            lds_barrier();
+            // 5a: norms, sigmoid and gate sums of the previous chunk
+            if (jc > 0) prep_a();
+            lds_barrier();
+            // 5b: its operand values; loads of the one before it
+            if (jc > 0) {
+                prep_b();
+                if (jc > 1) load_chunk(c0 - 2 * kChunk);
+            }
+            lds_barrier();
+        }
+    }
+}
+
+// ============================================================================
 // B2: chunk-parallel gradients
 // ============================================================================
 // One workgroup per (chunk, head), full value width.  Operand tiles live in LDS
@@ -1762,8 +2147,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParam
 // ============================================================================
 template <typename T, int DK>
 static hipError_t launch_scan(const BwdParams& p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.N * p.H * p.nslices)), block(kThreads);
-    hipLaunchKernelGGL((kda_bwd_scan_kernel<T, DK>), grid, block, 0, s, p);
+    const dim3 grid((unsigned)(p.N * p.H * p.nslices));
+    if constexpr (std::is_same<T, bf16>::value)
+        hipLaunchKernelGGL((kda_bwd_scan_bf16_kernel<DK>), grid, dim3(kWideThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((kda_bwd_scan_kernel<T, DK>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -458,19 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 // SIMD carries one wave of each group, so the prep waves' VALU work fills the
 // state waves' MFMA and LDS latency.
 // ============================================================================
-constexpr int kFwdThreads = 512;
-
-// Ktil^T tile of the bf16 kernel: rows c (key channel), 64 positions (chunk row
-// index r, permuted by perm32) per row, no padding; the 16-byte group of a
-// position is XOR-swizzled with (c ^ c>>3) & 7.  The A-fragment reads (16
-// consecutive rows) and the prep waves' writes (rows 8 apart) then spread over
-// the LDS banks.
-__device__ __forceinline__ int kt_off(int c, int pos) {
-    return c * kChunk + ((((pos >> 3) ^ (c ^ (c >> 3))) & 7) << 3) + (pos & 7);
-}
-
 template <typename TO, int DK, bool SAVE>
-__global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
     typedef bf16 T;
     __shared__ FwdSmem<T, DK> sm;
     typedef FwdSmem<T, DK> SM;
@@ -656,7 +645,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void kda_fwd_bf16_kernel(FwdParams 
     // The k32 steps of Aqk U read the upper 16x16 blocks (0,1) and (2,3) of the
     // Aqk tiles, which no chunk writes: clear them once.  (The first barrier
     // inside the chunk loop orders this before any read.)
-    for (int e = tid; e < kChunk * PC; e += kFwdThreads) {
+    for (int e = tid; e < kChunk * PC; e += kWideThreads) {
         sm.aqk[e] = from_f32<T>(0.f);
         sm.aqkl[e] = from_f32<T>(0.f);
     }
@@ -900,9 +889,9 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool save, hipStream_t s) {
     const dim3 grid((unsigned)(p.N * p.H * p.nslices));
     if constexpr (std::is_same<T, bf16>::value) {
         if (save)
-            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, true>), grid, dim3(kFwdThreads), 0, s, p);
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, true>), grid, dim3(kWideThreads), 0, s, p);
         else
-            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, false>), grid, dim3(kFwdThreads), 0, s, p);
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, false>), grid, dim3(kWideThreads), 0, s, p);
     } else {
         if (save)
             hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, true>), grid, dim3(kThreads), 0, s, p);

@@ -10,6 +10,15 @@ namespace kda {
 constexpr int kChunk = 64;      // tokens per chunk
 constexpr int kSlice = 64;      // value columns per forward / reverse-scan workgroup
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
+constexpr int kWideThreads = 512;   // 8 wave64: four state waves + four prep waves (bf16 kernels)
+
+// Transposed operand tile [row c][64 chunk positions] without padding, each
+// 16-byte group XOR-swizzled with (c ^ c>>3) & 7, so that A-fragment reads (16
+// consecutive rows) and writes from the prep layout (rows 8 apart) spread over
+// the LDS banks.  `pos` is the position inside the row (perm32 order).
+__device__ __forceinline__ int kt_off(int c, int pos) {
+    return c * kChunk + ((((pos >> 3) ^ (c ^ (c >> 3))) & 7) << 3) + (pos & 7);
+}
 
 // Per-chunk state slots: chunk j of sequence n uses slot floor(cu[n]/64) + n + j.
 // The map is collision-free and bounded by floor(T/64) + N (see kda_api.hip).
