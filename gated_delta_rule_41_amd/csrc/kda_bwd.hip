@@ -817,7 +817,8 @@ struct ChunkLds {
     static constexpr int DGC = GC + DK * 4;              // float[DK]
     static constexpr int RED = DGC + DK * 4;             // float[4][DK]
     static constexpr int DBV = RED + 4 * DK * 4;         // float[4][64]
-    static constexpr int BYTES = DBV + 4 * 64 * 4;
+    static constexpr int GW = DBV + 4 * 64 * 4;          // float[4][DK]: per-wave column sums of g
+    static constexpr int BYTES = GW + 4 * DK * 4;
     static_assert(BYTES <= 163840, "chunk kernel LDS");
 };
 
@@ -928,32 +929,39 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     // ================= prep (rows 16w+4qg+i, key cols CPL*cl+e) =================
-    RawRow<T, CPL> rq[4], rk[4];
-    float G[4][CPL], beta[4], nq[4], nk[4], GC[CPL];
-    {
+    // The raw rows and gate cumsums are not kept across the kernel (they would
+    // spill): prep_fill reloads them (L2-resident) and rebuilds G from the
+    // per-wave column sums of g, which the first call leaves in LDS.
+    float* const sgw = reinterpret_cast<float*>(lds + LY::GW);
+    struct Prep {
+        RawRow<T, CPL> q[4], k[4];
+        float G[4][CPL], GC[CPL], beta[4], iq[4], ik[4];
+    };
+    auto prep_fill = [&](Prep& P, bool first) {
         RawRow<T, CPL> rg[4];
-        float rb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * w + 4 * qg + i;
+            float rb = 0.f, nq = 1.f, nk = 1.f;
             if (r < L) {
-                rq[i].load(qc + r * rsk + CPL * cl);
-                rk[i].load(kc + r * rsk + CPL * cl);
+                P.q[i].load(qc + r * rsk + CPL * cl);
+                P.k[i].load(kc + r * rsk + CPL * cl);
                 rg[i].load(gcp + r * rsk + CPL * cl);
-                rb[i] = gload1(bc + (int64_t)r * H);
-                nq[i] = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
-                nk[i] = p.nk_saved[(c0 + r) * H + h];
+                rb = gload1(bc + (int64_t)r * H);
+                nq = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
+                nk = p.nk_saved[(c0 + r) * H + h];
             } else {
-                rq[i].zero(); rk[i].zero(); rg[i].zero();
-                rb[i] = 0.f; nq[i] = 1.f; nk[i] = 1.f;
+                P.q[i].zero(); P.k[i].zero(); rg[i].zero();
             }
-            beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
+            P.beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb)) : 0.f;
+            P.iq[i] = p.scale / nq;
+            P.ik[i] = 1.f / nk;
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
             float a = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { a += rg[i][e] * kLog2e; G[i][e] = a; }
+            for (int i = 0; i < 4; ++i) { a += rg[i][e] * kLog2e; P.G[i][e] = a; }
             const float tot = a;
             float s = tot, x;
             x = __shfl_up(s, 16);
@@ -962,40 +970,32 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             if (qg >= 2) s += x;
             const float excl = s - tot;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) G[i][e] += excl;
-            if (qg == 3) sred[w * DK + CPL * cl + e] = s;
+            for (int i = 0; i < 4; ++i) P.G[i][e] += excl;
+            if (first && qg == 3) sgw[w * DK + CPL * cl + e] = s;
         }
-    }
-    __syncthreads();
+        if (first) lds_barrier();
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-        const int c = CPL * cl + e;
-        float a = 0.f, tot = 0.f;
+        for (int e = 0; e < CPL; ++e) {
+            const int c = CPL * cl + e;
+            float a = 0.f, tot = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            const float x = sred[ww * DK + c];
-            if (ww < w) a += x;
-            tot += x;
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const float x = sgw[w2 * DK + c];
+                if (w2 < w) a += x;
+                tot += x;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) P.G[i][e] += a;
+            P.GC[e] = tot;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) G[i][e] += a;
-        GC[e] = tot;
-    }
-    if (w == 0 && qg == 0) {
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) sgc[CPL * cl + e] = fast_exp2(GC[e]);
-    }
-    if (cl == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sbeta[16 * w + 4 * qg + i] = beta[i];
-    }
+    };
     // prep-layout value of qh*Gam, beta*kh*Gam, kh/Gam, Ktil at (row i, col e)
-    auto vQG = [&](int i, int e) { return rq[i][e] * (p.scale / nq[i]) * fast_exp2(G[i][e]); };
-    auto vKG = [&](int i, int e) { return rk[i][e] * (beta[i] / nk[i]) * fast_exp2(G[i][e]); };
-    auto vKI = [&](int i, int e) { return rk[i][e] * (1.f / nk[i]) * fast_exp2(-G[i][e]); };
-    auto vKt = [&](int i, int e) { return rk[i][e] * (1.f / nk[i]) * fast_exp2(GC[e] - G[i][e]); };
+    auto vQG = [&](const Prep& P, int i, int e) { return P.q[i][e] * P.iq[i] * fast_exp2(P.G[i][e]); };
+    auto vKG = [&](const Prep& P, int i, int e) { return P.k[i][e] * (P.beta[i] * P.ik[i]) * fast_exp2(P.G[i][e]); };
+    auto vKI = [&](const Prep& P, int i, int e) { return P.k[i][e] * P.ik[i] * fast_exp2(-P.G[i][e]); };
+    auto vKt = [&](const Prep& P, int i, int e) { return P.k[i][e] * P.ik[i] * fast_exp2(P.GC[e] - P.G[i][e]); };
     // writers: row-major [r][c] tile (stride PK) or transposed [c][perm32(r)] tile (stride PC)
-    auto put_rm = [&](T* hi, T* lo, auto val, bool split) {
+    auto put_rm = [&](const Prep& P, T* hi, T* lo, auto val, bool split) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * w + 4 * qg + i;
@@ -1003,28 +1003,41 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             for (int e4 = 0; e4 < CPL; e4 += 4) {
                 f32x4 x;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = val(i, e4 + j);
+                for (int j = 0; j < 4; ++j) x[j] = val(P, i, e4 + j);
                 const int o = r * PK + CPL * cl + e4;
                 if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
                 else sts4<T>(hi + o, x);
             }
         }
     };
-    auto put_tp = [&](T* hi, T* lo, auto val, bool split, bool perm) {
+    auto put_tp = [&](const Prep& P, T* hi, T* lo, auto val, bool split, bool perm) {
         const int r0 = 16 * w + 4 * qg;
         const int pr = perm ? perm32(r0) : r0;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            f32x4 x = {val(0, e), val(1, e), val(2, e), val(3, e)};
+            f32x4 x = {val(P, 0, e), val(P, 1, e), val(P, 2, e), val(P, 3, e)};
             const int o = (CPL * cl + e) * PC + pr;
             if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
             else sts4<T>(hi + o, x);
         }
     };
-    put_rm(S(0), S(1), vQG, true);    // QG  h/l
-    put_rm(S(2), S(3), vKI, true);    // KI  h/l
-    put_rm(S(4), S(4), vKG, false);   // KG  h
-    __syncthreads();
+    f32x4 Wc[NBK][4], U[NBV][4];
+    RawRow<T, VPL> ddr[4];   // dO rows of this lane, staged row-major in LDS for the dO products
+    {
+    Prep P;
+    prep_fill(P, true);
+    if (w == 0 && qg == 0) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) sgc[CPL * cl + e] = fast_exp2(P.GC[e]);
+    }
+    if (cl == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sbeta[16 * w + 4 * qg + i] = P.beta[i];
+    }
+    put_rm(P, S(0), S(1), vQG, true);    // QG  h/l
+    put_rm(P, S(2), S(3), vKI, true);    // KI  h/l
+    put_rm(P, S(4), S(4), vKG, false);   // KG  h
+    lds_barrier();
 
     // ================= Akk (fp32 -> slot 5), Aqk^T h/l (slot 6) =================
     float* const Af = Sf(5);
@@ -1051,7 +1064,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             put_blk<T, SPLIT>(S(6), Sh(6), PC, 16 * mb, nb, b, qg, cl, false);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ================= T = (I + Akk)^{-1} (fp32 in slot 7) =================
     float* const Tf = Sf(7);
     {
@@ -1067,7 +1080,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Tf[(16 * w + 4 * qg + i) * PF + 16 * w + cl] = tw[i];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
         // tmp_ij = sum_{k=j}^{i-1} Akk_ik T_kj in the (unused) upper block (j, i) of Af
@@ -1079,7 +1092,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
                 for (int t = 0; t < 16; ++t) s += Af[(16 * i + a) * PF + 16 * k + t] * Tf[(16 * k + t) * PF + 16 * j + bb];
             Af[(16 * j + a) * PF + 16 * i + bb] = s;
         }
-        __syncthreads();
+        lds_barrier();
         for (int idx = tid; idx < (4 - d) * 256; idx += kThreads) {
             const int j = idx >> 8, i = j + d, a = (idx >> 4) & 15, bb = idx & 15;
             float s = 0.f;
@@ -1087,7 +1100,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             for (int t = 0; t < 16; ++t) s += Tf[(16 * i + a) * PF + 16 * i + t] * Af[(16 * j + t) * PF + 16 * i + bb];
             Tf[(16 * i + a) * PF + 16 * j + bb] = -s;
         }
-        __syncthreads();
+        lds_barrier();
     }
     // T tiles: Trm [r][s] (slot 5 first half), T diag(beta) [r][s] h/l (slot 5 second half, slot 0
     // second half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1); V^T, dO^T [j][r] (slots 2, 3)
@@ -1107,25 +1120,24 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             if constexpr (SPLIT) Tbl[r * PC + c] = from_f32<T>(tb - to_f32(tbh));
             Ttp[c * PC + perm32(r)] = from_f32<T>(t);
         }
-        put_tp(S(1), S(1), vKG, false, false);
+        put_tp(P, S(1), S(1), vKG, false, false);
         const int r0 = 16 * w + 4 * qg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            RawRow<T, VPL> vv, dd;
-            if (r < L) { vv.load(vc + r * rsv + VPL * cl); dd.load(doc + r * rsv + VPL * cl); }
-            else { vv.zero(); dd.zero(); }
+            RawRow<T, VPL> vv;
+            if (r < L) { vv.load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
+            else { vv.zero(); ddr[i].zero(); }
 #pragma unroll
             for (int e = 0; e < VPL; ++e) {
                 S(2)[(VPL * cl + e) * PC + r] = from_f32<T>(vv[e]);
-                S(3)[(VPL * cl + e) * PC + r] = from_f32<T>(dd[e]);
+                S(3)[(VPL * cl + e) * PC + r] = from_f32<T>(ddr[i][e]);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= W = T KG, Ut = T diag(beta) v =================
-    f32x4 Wc[NBK][4], U[NBV][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -1151,14 +1163,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             }
             U[t][mb] = a;
         }
-    __syncthreads();
+    lds_barrier();
     // W rm (slot 4), Ktil rm h/l (slots 7, 2)
 #pragma unroll
     for (int t = 0; t < NBK; ++t)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(4), S(4), PK, 16 * mb, 16 * (w + 4 * t), Wc[t][mb], qg, cl, true);
-    put_rm(S(7), S(2), vKt, true);
-    __syncthreads();
+    put_rm(P, S(7), S(2), vKt, true);
+    }
+    lds_barrier();
     // ================= U = Ut - W S0;  dU = Aqk^T dO + Ktil dS1 =================
     f32x4 dU[NBV][4];
 #pragma unroll
@@ -1191,8 +1204,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
                 if constexpr (SPLIT) dU[t][mb] = mma_k32(dU[t][mb], lds8<T>(Sh(6) + ka), bo);
             }
     }
-    __syncthreads();
-    // U rm h/l (slots 4, 3), dU rm (slot 7)
+    lds_barrier();
+    // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (16 * w + 4 * qg + i) * PV + VPL * cl) = ddr[i].x;
 #pragma unroll
     for (int t = 0; t < NBV; ++t)
 #pragma unroll
@@ -1200,7 +1215,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * (w + 4 * t), U[t][mb], qg, cl, true);
             put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * (w + 4 * t), dU[t][mb], qg, cl, true);
         }
-    __syncthreads();
+    lds_barrier();
 
     // ================= dBV = T^T dU  ->  dv, dbeta (v part) =================
     {
@@ -1261,10 +1276,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             else vb = V8T{};
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const int r = 16 * mb + cl;
-                V8T da;
-                if (r < L) da = gin8(doc + r * rsv + 32 * kk + 8 * qg);
-                else da = V8T{};
+                const V8T da = lds8<T>(S(6) + (16 * mb + cl) * PV + 32 * kk + 8 * qg);
                 dAqk[mb] = mma_k32(dAqk[mb], da, uh);
                 if constexpr (SPLIT) dAqk[mb] = mma_k32(dAqk[mb], da, ul);
                 dT[mb] = mma_k32(dT[mb], lds8<T>(S(7) + (16 * mb + cl) * PV + 32 * kk + 8 * qg), vb);
@@ -1298,9 +1310,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int r = 16 * mb + cl;
-                V8T da;
-                if (r < L) da = gin8(doc + r * rsv + 32 * kk + 8 * qg);
-                else da = V8T{};
+                const V8T da = lds8<T>(S(6) + r * PV + 32 * kk + 8 * qg);
                 dQG[t][mb] = mma_k32(dQG[t][mb], da, sh);
                 if constexpr (SPLIT) dQG[t][mb] = mma_k32(dQG[t][mb], da, sl);
                 const int ka = r * PV + 32 * kk + 8 * qg;
@@ -1326,14 +1336,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
         if (part == 0) sdgc[c] = s;
     }
-    __syncthreads();
+    lds_barrier();
+    {
+    Prep P;
+    prep_fill(P, false);
     // dW rm (slot 2), KG rm (slot 6)
 #pragma unroll
     for (int t = 0; t < NBK; ++t)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(2), S(2), PK, 16 * mb, 16 * (w + 4 * t), dW[t][mb], qg, cl, true);
-    put_rm(S(6), S(6), vKG, false);
-    __syncthreads();
+    put_rm(P, S(6), S(6), vKG, false);
+    lds_barrier();
     // ================= dT += dW KG^T;  X = T^T dT -> slot 0 (2nd half) =================
     {
         const int nb = 16 * w;
@@ -1355,7 +1368,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, x, qg, cl, true);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // ================= dAkk = -strict(X T^T) =================
     f32x4 dAkk[4];
     {
@@ -1375,7 +1388,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             dAkk[mb] = a;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // tiles for the last products:
     //   dAkk rm [r][s] (slot 0, 2nd half), dAkk^T [s][r] (QX), dAqk rm h/l (slot 3),
     //   dAqk^T h/l (slot 7), KI^T h/l [c][s] (slots 2, 6), QG^T h/l [c][r] (slots 4, 5)
@@ -1388,10 +1401,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             put_blk<T, SPLIT>(S(3), Sh(3), PC, 16 * mb, nb, dAqk[mb], qg, cl, true);
             put_blk<T, SPLIT>(S(7), Sh(7), PC, 16 * mb, nb, dAqk[mb], qg, cl, false);
         }
-        put_tp(S(2), S(6), vKI, true, false);
-        put_tp(S(4), S(5), vQG, true, false);
+        put_tp(P, S(2), S(6), vKI, true, false);
+        put_tp(P, S(4), S(5), vQG, true, false);
     }
-    __syncthreads();
+    }
+    lds_barrier();
     // ================= dKG = T^T dW + dAkk KI;  dQG += dAqk KI;  dKI = dAkk^T KG + dAqk^T QG =================
     f32x4 dKG[NBK][4], dKI[NBK][4];
 #pragma unroll
@@ -1420,7 +1434,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             dKI[t][mb] = ki;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= back to the prep layout (fp32 through LDS) =================
     constexpr int LDF = DK + 4;
@@ -1438,7 +1452,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             st_blk(F1, LDF, 16 * mb, nb, dKG[t][mb], qg, cl);
             st_blk(F2, LDF, 16 * mb, nb, dKI[t][mb], qg, cl);
         }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1448,32 +1462,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             gKG[i][e] = F1[o];
             gKI[i][e] = F2[o];
         }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int t = 0; t < NBK; ++t)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) st_blk(F0, LDF, 16 * mb, 16 * (w + 4 * t), dKt[t][mb], qg, cl);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < CPL; ++e) gKt[i][e] = F0[(16 * w + 4 * qg + i) * LDF + CPL * cl + e];
 
     // ================= chain rule to qh, kh, beta, G =================
+    Prep P;
+    prep_fill(P, false);
     float dqh[4][CPL], dkh[4][CPL], dG[4][CPL], dbk[4], colp[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) colp[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         dbk[i] = 0.f;
-        const float aq = p.scale / nq[i], ai = 1.f / nk[i];
+        const float aq = P.iq[i], ai = P.ik[i];
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            const float gam = fast_exp2(G[i][e]), gin = fast_exp2(-G[i][e]), ek = fast_exp2(GC[e] - G[i][e]);
-            const float qh = rq[i][e] * aq, kh = rk[i][e] * ai;
-            const float QG = qh * gam, KGv = beta[i] * kh * gam, KIv = kh * gin, Ktv = kh * ek;
+            const float gam = fast_exp2(P.G[i][e]), gin = fast_exp2(-P.G[i][e]), ek = fast_exp2(P.GC[e] - P.G[i][e]);
+            const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
+            const float QG = qh * gam, KGv = P.beta[i] * kh * gam, KIv = kh * gin, Ktv = kh * ek;
             dqh[i][e] = gQ[i][e] * gam;
-            dkh[i][e] = beta[i] * gam * gKG[i][e] + gKI[i][e] * gin + gKt[i][e] * ek;
+            dkh[i][e] = P.beta[i] * gam * gKG[i][e] + gKI[i][e] * gin + gKt[i][e] * ek;
             dG[i][e] = gQ[i][e] * QG + gKG[i][e] * KGv - gKI[i][e] * KIv - gKt[i][e] * Ktv;
             dbk[i] += gKG[i][e] * kh * gam;
             colp[e] += gKt[i][e] * Ktv;
@@ -1486,14 +1502,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         s += __shfl_xor(s, 32);
         if (qg == 0) sred[w * DK + CPL * cl + e] = s;
     }
-    __syncthreads();
+    lds_barrier();
     float dGC[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
         const int c = CPL * cl + e;
         dGC[e] = sred[c] + sred[DK + c] + sred[2 * DK + c] + sred[3 * DK + c] + sdgc[c] * sgc[c];
     }
-    __syncthreads();
+    lds_barrier();
     {
         float suf[CPL];
 #pragma unroll
@@ -1510,7 +1526,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             suf[e] = s - tot;
             if (qg == 0) sred[w * DK + CPL * cl + e] = s;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
             const int c = CPL * cl + e;
@@ -1530,10 +1546,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * qg + i;
-        const float aq = p.scale / nq[i], ai = 1.f / nk[i];
+        const float aq = P.iq[i], ai = P.ik[i];
         float sq = 0.f, sk = 0.f, db = dbk[i];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * aq * dqh[i][e]; sk += rk[i][e] * ai * dkh[i][e]; }
+        for (int e = 0; e < CPL; ++e) { sq += P.q[i][e] * aq * dqh[i][e]; sk += P.k[i][e] * ai * dkh[i][e]; }
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); db += __shfl_xor(db, m); }
         if (r < L) {
@@ -1542,14 +1558,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
                 const int64_t off = r * rsk + CPL * cl + e;
-                const float qh = rq[i][e] * aq, kh = rk[i][e] * ai;
+                const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
                 dqp[off] = from_f32<TO>(aq * (dqh[i][e] - qh * qdot));
                 dkp[off] = from_f32<TO>(ai * (dkh[i][e] - kh * sk));
                 dgp[off] = from_f32<TO>(dG[i][e]);
             }
             if (cl == 0) {
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
-                dbp[(int64_t)r * H] = from_f32<TO>(dbeta * beta[i] * (1.f - beta[i]));
+                dbp[(int64_t)r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
             }
         }
     }
