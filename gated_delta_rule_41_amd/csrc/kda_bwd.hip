@@ -885,6 +885,19 @@ __device__ __forceinline__ void put_blk_tp(T* hi, T* lo, int ld, int m0, int n0,
     sts4_split<T, SPLIT>(hi + o, lo + (SPLIT ? o : 0), x);
 }
 
+// N contiguous outputs from fp32 values, as 16-byte stores.
+template <typename TO, int N>
+__device__ __forceinline__ void store_row(TO* p, const float (&v)[N]) {
+    if constexpr (sizeof(TO) == 4) {
+#pragma unroll
+        for (int j = 0; j < N; j += 4) *reinterpret_cast<f32x4*>(p + j) = f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; j += 4)
+            *reinterpret_cast<bf16x4*>(p + j) = pack4<bf16>(f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]});
+    }
+}
+
 template <typename T, typename TO, int DK, int DV>
 __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p) {
     typedef ChunkLds<T, DK, DV> LY;
@@ -1022,7 +1035,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         }
     };
     f32x4 Wc[NBK][4], U[NBV][4];
-    RawRow<T, VPL> ddr[4];   // dO rows of this lane, staged row-major in LDS for the dO products
+    RawRow<T, VPL> ddr[4], vvr[4];   // dO and v rows of this lane, staged row-major in LDS later
     {
     Prep P;
     prep_fill(P, true);
@@ -1081,27 +1094,32 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         for (int i = 0; i < 4; ++i) Tf[(16 * w + 4 * qg + i) * PF + 16 * w + cl] = tw[i];
     }
     lds_barrier();
+    // off-diagonal blocks, column j on wave j: T_ij = -T_ii sum_{k=j}^{i-1} Akk_ik T_kj
+    // (fp32 MFMA; the column's blocks stay in accumulator layout, which is the
+    // B fragment of the next step)
+    {
+        auto solve_col = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            f32x4 col[4];
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        // tmp_ij = sum_{k=j}^{i-1} Akk_ik T_kj in the (unused) upper block (j, i) of Af
-        for (int idx = tid; idx < (4 - d) * 256; idx += kThreads) {
-            const int j = idx >> 8, i = j + d, a = (idx >> 4) & 15, bb = idx & 15;
-            float s = 0.f;
-            for (int k = j; k < i; ++k)
+            for (int i = 0; i < 4; ++i) col[j][i] = Tf[(16 * j + 4 * qg + i) * PF + 16 * j + cl];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) s += Af[(16 * i + a) * PF + 16 * k + t] * Tf[(16 * k + t) * PF + 16 * j + bb];
-            Af[(16 * j + a) * PF + 16 * i + bb] = s;
-        }
-        lds_barrier();
-        for (int idx = tid; idx < (4 - d) * 256; idx += kThreads) {
-            const int j = idx >> 8, i = j + d, a = (idx >> 4) & 15, bb = idx & 15;
-            float s = 0.f;
+            for (int i = j + 1; i < 4; ++i) {
+                f32x4 acc = zero;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) s += Tf[(16 * i + a) * PF + 16 * i + t] * Af[(16 * j + t) * PF + 16 * i + bb];
-            Tf[(16 * i + a) * PF + 16 * j + bb] = -s;
-        }
-        lds_barrier();
+                for (int k = j; k < i; ++k)
+                    acc = mma_k16(acc, *reinterpret_cast<const f32x4*>(&Af[(16 * i + cl) * PF + 16 * k + 4 * qg]), col[k]);
+                const f32x4 tii = *reinterpret_cast<const f32x4*>(&Tf[(16 * i + cl) * PF + 16 * i + 4 * qg]);
+                col[i] = -mma_k16(zero, tii, acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tf[(16 * i + 4 * qg + r) * PF + 16 * j + cl] = col[i][r];
+            }
+        };
+        if (w == 0) solve_col(std::integral_constant<int, 0>{});
+        else if (w == 1) solve_col(std::integral_constant<int, 1>{});
+        else if (w == 2) solve_col(std::integral_constant<int, 2>{});
     }
+    lds_barrier();
     // T tiles: Trm [r][s] (slot 5 first half), T diag(beta) [r][s] h/l (slot 5 second half, slot 0
     // second half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1); V^T, dO^T [j][r] (slots 2, 3)
     {
@@ -1125,12 +1143,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            RawRow<T, VPL> vv;
-            if (r < L) { vv.load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
-            else { vv.zero(); ddr[i].zero(); }
+            if (r < L) { vvr[i].load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
+            else { vvr[i].zero(); ddr[i].zero(); }
 #pragma unroll
             for (int e = 0; e < VPL; ++e) {
-                S(2)[(VPL * cl + e) * PC + r] = from_f32<T>(vv[e]);
+                S(2)[(VPL * cl + e) * PC + r] = from_f32<T>(vvr[i][e]);
                 S(3)[(VPL * cl + e) * PC + r] = from_f32<T>(ddr[i][e]);
             }
         }
@@ -1205,9 +1222,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             }
     }
     lds_barrier();
-    // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6)
+    // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6), v rm (slot 2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (16 * w + 4 * qg + i) * PV + VPL * cl) = ddr[i].x;
+    for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (16 * w + 4 * qg + i) * PV + VPL * cl) = ddr[i].x;
+        *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (16 * w + 4 * qg + i) * PV + VPL * cl) = vvr[i].x;
+    }
 #pragma unroll
     for (int t = 0; t < NBV; ++t)
 #pragma unroll
@@ -1245,7 +1265,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
                     const int r = 16 * mb + 4 * qg + i;
                     if (r < L) {
                         dvp[r * rsv + nc] = from_f32<TO>(sbeta[r] * a[i]);
-                        rowpart[mb][i] += gload1(vc + r * rsv + nc) * a[i];
+                        rowpart[mb][i] += to_f32(S(2)[r * PV + nc]) * a[i];
                     }
                 }
             }
@@ -1254,9 +1274,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s = rowpart[mb][i];
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) s += __shfl_xor(s, m);
+                const float s = row16_sum(rowpart[mb][i]);
                 if (cl == 0) sdbv[w * 64 + 16 * mb + 4 * qg + i] = s;
             }
     }
@@ -1264,16 +1282,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     f32x4 dAqk[4], dT[4];
     {
         const int nb = 16 * w;
-        const bool rowok = nb + cl < L;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) { dAqk[mb] = zero; dT[mb] = zero; }
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
             const int kb = (nb + cl) * PV + 32 * kk + 8 * qg;
             const V8T uh = lds8<T>(S(4) + kb), ul = lds8<T>(S(3) + (SPLIT ? kb : 0));
-            V8T vb;
-            if (rowok) vb = gin8(vc + (nb + cl) * rsv + 32 * kk + 8 * qg);
-            else vb = V8T{};
+            const V8T vb = lds8<T>(S(2) + kb);   // rows past the chunk end are zero
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const V8T da = lds8<T>(S(6) + (16 * mb + cl) * PV + 32 * kk + 8 * qg);
@@ -1299,14 +1314,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         const int nr = 16 * (w + 4 * t) + cl;   // key row of S0 / dS1 feeding this lane
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) { dQG[t][mb] = zero; dW[t][mb] = zero; dKt[t][mb] = zero; }
+        float gpart = 0.f;   // this lane's share of dL/dGam_C[nr] = sum_j S0[nr][j] dS1[nr][j]
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
-            float x[8];
+            float xs[8], xd[8];
             V8T sh, sl, dh, dl;
-            gf8(x, S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-            if constexpr (SPLIT) cvt8(x, sh, sl); else cvt8(x, sh);
-            gf8(x, dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-            if constexpr (SPLIT) cvt8(x, dh, dl); else cvt8(x, dh);
+            gf8(xs, S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            gf8(xd, dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gpart += xs[j] * xd[j];
+            if constexpr (SPLIT) cvt8(xs, sh, sl); else cvt8(xs, sh);
+            if constexpr (SPLIT) cvt8(xd, dh, dl); else cvt8(xd, dh);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int r = 16 * mb + cl;
@@ -1321,20 +1339,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) dW[t][mb] = -dW[t][mb];
-    }
-    {
-        // dL/dGam_C[c] = sum_j S0[c][j] dS1[c][j]
-        constexpr int TPR = kThreads / DK;
-        const int c = tid / TPR, part = tid % TPR;
-        float s = 0.f;
-        for (int j = part * 4; j < DV; j += TPR * 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + j);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(dS1 + (int64_t)c * DV + j);
-            s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-        }
-#pragma unroll
-        for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
-        if (part == 0) sdgc[c] = s;
+        gpart += __shfl_xor(gpart, 16);
+        gpart += __shfl_xor(gpart, 32);
+        if (qg == 0) sdgc[nr] = gpart;
     }
     lds_barrier();
     {
@@ -1547,22 +1554,26 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * qg + i;
         const float aq = P.iq[i], ai = P.ik[i];
-        float sq = 0.f, sk = 0.f, db = dbk[i];
+        float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) { sq += P.q[i][e] * aq * dqh[i][e]; sk += P.k[i][e] * ai * dkh[i][e]; }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); db += __shfl_xor(db, m); }
+        sq = row16_sum(sq);
+        sk = row16_sum(sk);
+        const float db = row16_sum(dbk[i]);
         if (r < L) {
             const float sc = p.scale;
             const float qdot = sc != 0.f ? sq / (sc * sc) : 0.f;   // (qh . dqh) / scale^2
+            float vq[CPL], vk[CPL];
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-                const int64_t off = r * rsk + CPL * cl + e;
                 const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
-                dqp[off] = from_f32<TO>(aq * (dqh[i][e] - qh * qdot));
-                dkp[off] = from_f32<TO>(ai * (dkh[i][e] - kh * sk));
-                dgp[off] = from_f32<TO>(dG[i][e]);
+                vq[e] = aq * (dqh[i][e] - qh * qdot);
+                vk[e] = ai * (dkh[i][e] - kh * sk);
             }
+            const int64_t off = r * rsk + CPL * cl;
+            store_row<TO, CPL>(dqp + off, vq);
+            store_row<TO, CPL>(dkp + off, vk);
+            store_row<TO, CPL>(dgp + off, dG[i]);
             if (cl == 0) {
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
                 dbp[(int64_t)r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
