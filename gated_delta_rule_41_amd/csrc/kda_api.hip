@@ -67,8 +67,15 @@ kda_status opt_ptr(const void* p, const char* name) {
     return KDA_OK;
 }
 
+// Per-chunk U (forward) and dU (reverse scan), fp32 [slots, H, 64, dv]: the
+// bf16 chunk-gradient kernel reads them instead of recomputing both.
+size_t chunk_u_bytes(const kda_config* c, int64_t T, int32_t N) {
+    if (c->in_dtype != KDA_BF16) return 0;
+    return (size_t)kda::num_slots(T, N) * c->H * kda::kChunk * c->dv * sizeof(float);
+}
+
 struct SavedLayout {
-    size_t states, nq, nk, total;
+    size_t states, nq, nk, u, total;
 };
 
 SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
@@ -78,8 +85,14 @@ SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
     s.states = 0;
     s.nq = align256(st);
     s.nk = s.nq + align256(nrm);
-    s.total = s.nk + align256(nrm);
+    s.u = s.nk + align256(nrm);
+    s.total = s.u + align256(chunk_u_bytes(c, T, N));
     return s;
+}
+
+// dL/dS at the end of every chunk (state type), then dU of every chunk.
+size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
+    return align256((size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c));
 }
 
 }  // namespace
@@ -118,8 +131,7 @@ size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
 
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
     if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
-    // dL/dS at the end of every chunk, same storage type as the saved states
-    return align256((size_t)kda::num_slots(T, N) * cfg->H * cfg->dk * cfg->dv * state_elem_bytes(cfg));
+    return bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N));
 }
 
 kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
@@ -156,6 +168,7 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
         p.st_saved = base + L.states;
         p.nq_saved = (float*)(base + L.nq);
         p.nk_saved = (float*)(base + L.nk);
+        p.u_saved = chunk_u_bytes(cfg, T, N) ? (float*)(base + L.u) : nullptr;
     }
     p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
     p.seqlen = cu ? 0 : (int32_t)(T / N);
@@ -206,6 +219,10 @@ kda_status kda_bwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     p.nk_saved = (const float*)(base + L.nk);
     p.dO = dO; p.dS_final = dSf;
     p.dst_saved = workspace;
+    if (chunk_u_bytes(cfg, T, N)) {
+        p.u_saved = (const float*)(base + L.u);
+        p.du_ws = (float*)((char*)workspace + bwd_dst_bytes(cfg, T, N));
+    }
     p.dq = dq; p.dk = dk; p.dv_out = dv; p.dg = dg; p.db = dbeta; p.dS0 = dS0;
     p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
     p.seqlen = cu ? 0 : (int32_t)(T / N);

@@ -657,6 +657,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 }
                 duf[0] = pack8<T>(dU[0], dU[1]);
                 duf[1] = pack8<T>(dU[2], dU[3]);
+                // dU of this chunk (fp32), for the chunk-parallel gradients
+                float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv + vcol;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ub[(int64_t)(16 * i + 4 * qg + j) * dv] = dU[i][j];
             }
             lds_barrier();
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
@@ -1034,11 +1040,33 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             else sts4<T>(hi + o, x);
         }
     };
-    f32x4 Wc[NBK][4], U[NBV][4];
+    // U (saved by the forward) and dU (left by the reverse scan) of this chunk,
+    // in accumulator layout: rows 16mb+4qg+i, value column 16(w+4t)+cl
+    f32x4 U[NBV][4], dU[NBV][4];
     RawRow<T, VPL> ddr[4], vvr[4];   // dO and v rows of this lane, staged row-major in LDS later
     {
     Prep P;
     prep_fill(P, true);
+    {
+        const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
+        const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
+#pragma unroll
+        for (int t = 0; t < NBV; ++t)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * (w + 4 * t) + cl;
+                    U[t][mb][i] = ub[o];
+                    dU[t][mb][i] = dub[o];
+                }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * qg + i;
+            if (r < L) { vvr[i].load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
+            else { vvr[i].zero(); ddr[i].zero(); }
+        }
+    }
     if (w == 0 && qg == 0) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) sgc[CPL * cl + e] = fast_exp2(P.GC[e]);
@@ -1047,34 +1075,27 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sbeta[16 * w + 4 * qg + i] = P.beta[i];
     }
-    put_rm(P, S(0), S(1), vQG, true);    // QG  h/l
-    put_rm(P, S(2), S(3), vKI, true);    // KI  h/l
+    put_rm(P, S(2), S(2), vKI, false);   // KI  h
     put_rm(P, S(4), S(4), vKG, false);   // KG  h
     lds_barrier();
 
-    // ================= Akk (fp32 -> slot 5), Aqk^T h/l (slot 6) =================
+    // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
     {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            f32x4 a = zero, b = zero;
+            f32x4 a = zero;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int ka = (16 * mb + cl) * PK + 32 * kk + 8 * qg, kb = (nb + cl) * PK + 32 * kk + 8 * qg;
-                const V8T ki_h = lds8<T>(S(2) + kb);
-                a = mma_k32(a, lds8<T>(S(4) + ka), ki_h);
-                b = mma3<SPLIT>(b, lds8<T>(S(0) + ka), lds8<T>(S(1) + ka), ki_h, lds8<T>(S(3) + kb));
+                a = mma_k32(a, lds8<T>(S(4) + ka), lds8<T>(S(2) + kb));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mb + 4 * qg + i, s = nb + cl;
-                a[i] = s < r ? a[i] : 0.f;
-                b[i] = s <= r ? b[i] : 0.f;
-                Af[r * PF + s] = a[i];
+                Af[r * PF + s] = s < r ? a[i] : 0.f;
             }
-            // Aqk^T tile [s][r] (plain index order)
-            put_blk<T, SPLIT>(S(6), Sh(6), PC, 16 * mb, nb, b, qg, cl, false);
         }
     }
     lds_barrier();
@@ -1120,106 +1141,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         else if (w == 2) solve_col(std::integral_constant<int, 2>{});
     }
     lds_barrier();
-    // T tiles: Trm [r][s] (slot 5 first half), T diag(beta) [r][s] h/l (slot 5 second half, slot 0
-    // second half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1); V^T, dO^T [j][r] (slots 2, 3)
+    // T tiles: Trm [r][s] (slot 5 first half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1)
     {
         T* const Trm = S(5);
-        T* const Tb = Sh(5);
-        T* const Tbl = Sh(0);
         T* const Ttp = S(0);
         for (int e = tid; e < kChunk * kChunk; e += kThreads) {
             const int r = e >> 6, c = e & 63;
             const float t = Tf[r * PF + c];
             Trm[r * PC + c] = from_f32<T>(t);
-            // the diagonal of T diag(beta) is beta itself: its rounding would show in U
-            const float tb = t * sbeta[c];
-            const T tbh = from_f32<T>(tb);
-            Tb[r * PC + c] = tbh;
-            if constexpr (SPLIT) Tbl[r * PC + c] = from_f32<T>(tb - to_f32(tbh));
             Ttp[c * PC + perm32(r)] = from_f32<T>(t);
         }
         put_tp(P, S(1), S(1), vKG, false, false);
-        const int r0 = 16 * w + 4 * qg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i;
-            if (r < L) { vvr[i].load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
-            else { vvr[i].zero(); ddr[i].zero(); }
-#pragma unroll
-            for (int e = 0; e < VPL; ++e) {
-                S(2)[(VPL * cl + e) * PC + r] = from_f32<T>(vvr[i][e]);
-                S(3)[(VPL * cl + e) * PC + r] = from_f32<T>(ddr[i][e]);
-            }
-        }
     }
-    lds_barrier();
-
-    // ================= W = T KG, Ut = T diag(beta) v =================
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int t = 0; t < NBK; ++t) {
-            f32x4 a = zero;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                a = mma_k32(a, lds8<T>(S(5) + (16 * mb + cl) * PC + 32 * kk + 8 * qg),
-                            lds8<T>(S(1) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg));
-            Wc[t][mb] = a;
-        }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int t = 0; t < NBV; ++t) {
-            f32x4 a = zero;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg;
-                const V8T bv = lds8<T>(S(2) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg);
-                a = mma_k32(a, lds8<T>(Sh(5) + ka), bv);
-                if constexpr (SPLIT) a = mma_k32(a, lds8<T>(Sh(0) + ka), bv);
-            }
-            U[t][mb] = a;
-        }
-    lds_barrier();
-    // W rm (slot 4), Ktil rm h/l (slots 7, 2)
-#pragma unroll
-    for (int t = 0; t < NBK; ++t)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(4), S(4), PK, 16 * mb, 16 * (w + 4 * t), Wc[t][mb], qg, cl, true);
-    put_rm(P, S(7), S(2), vKt, true);
-    }
-    lds_barrier();
-    // ================= U = Ut - W S0;  dU = Aqk^T dO + Ktil dS1 =================
-    f32x4 dU[NBV][4];
-#pragma unroll
-    for (int t = 0; t < NBV; ++t) {
-        const int nc = 16 * (w + 4 * t) + cl;   // value column of this lane's B fragments
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            float x[8];
-            V8T bs, bd, bdl;
-            gs8(x, S0 + (int64_t)(32 * kk + 8 * qg) * DV + nc, DV);
-            cvt8(x, bs);
-            gs8(x, dS1 + (int64_t)(32 * kk + 8 * qg) * DV + nc, DV);
-            if constexpr (SPLIT) cvt8(x, bd, bdl); else cvt8(x, bd);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int ka = (16 * mb + cl) * PK + 32 * kk + 8 * qg;
-                f32x4 uu = mma_k32(zero, lds8<T>(S(4) + ka), bs);
-                U[t][mb] -= uu;
-                if (kk == 0) dU[t][mb] = zero;
-                dU[t][mb] = mma3<SPLIT>(dU[t][mb], lds8<T>(S(7) + ka), lds8<T>(S(2) + (SPLIT ? ka : 0)), bd, SPLIT ? bdl : bd);
-            }
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg;
-                const V8T bo = lds8<T>(S(3) + (16 * (w + 4 * t) + cl) * PC + 32 * kk + 8 * qg);
-                dU[t][mb] = mma_k32(dU[t][mb], lds8<T>(S(6) + ka), bo);
-                if constexpr (SPLIT) dU[t][mb] = mma_k32(dU[t][mb], lds8<T>(Sh(6) + ka), bo);
-            }
     }
     lds_barrier();
     // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6), v rm (slot 2)

@@ -762,6 +762,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                     }
                 }
             }
+            if (SAVE) {
+                // U of this chunk (fp32), for the chunk-parallel gradients
+                float* ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * dv + vcol;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ub[(int64_t)(16 * i + 4 * qg + j) * dv] = Ut[i][j];
+            }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
             lds_barrier();

@@ -93,8 +93,11 @@ void kda_config_init(kda_config* cfg, int32_t H, int32_t dk, int32_t dv);
 
 /* Sizes in bytes (pure host functions; 0 for an invalid config).
  * kda_saved_size: the buffer kda_fwd fills under KDA_FLAG_SAVE_FOR_BWD and
- * kda_bwd reads: per-chunk entering states plus the per-token q/k norms.
- * kda_fwd_workspace_size / kda_bwd_workspace_size: scratch for one call. */
+ * kda_bwd reads: per-chunk entering states (fp32), the per-token q/k norms
+ * and, for bf16 inputs, each chunk's pseudo-values U = T beta v - W S (fp32).
+ * kda_fwd_workspace_size / kda_bwd_workspace_size: scratch for one call (the
+ * backward's holds dL/dS at the end of every chunk and, for bf16 inputs, each
+ * chunk's dL/dU). */
 size_t kda_saved_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);

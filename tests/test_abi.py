@@ -42,8 +42,9 @@ def test_sizes():
     states = slots * 32 * 128 * 128 * 4
     nrm = T * 32 * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm)
-    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states)
+    u = slots * 32 * 64 * 128 * 4   # per-chunk U (saved) and dU (workspace), bf16 inputs only
+    assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm) + al(u)
+    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states) + al(u)
     assert _lib.kda_fwd_workspace_size(cfg, T, N) == 0
     cfg32 = _lib.make_config(2, 64, 64, KDA_F32, KDA_F32)
     assert _lib.kda_saved_size(cfg32, 256, 1) == al(5 * 2 * 64 * 64 * 4) + 2 * al(256 * 2 * 4)
