@@ -4,20 +4,23 @@ Workload: B=4 packed sequences x T=8192 tokens, H=32 heads, dk=dv=128, chunk 64,
 bf16 inputs (q, k, v, g, beta logit, dO), fp32 state, fp32 outputs and
 gradients; seeded synthetic inputs from kda_inputs (the same recipe the parity
 tests use).  One step = one training pass of the whole hot path: kda_fwd with
-the state save, then kda_bwd (reverse state scan + chunk-parallel gradients).
+the state save, then kda_bwd as its two stages (kda_bwd_scan: reverse state
+scan; kda_bwd_grads: chunk-parallel gradients), one kernel each.
 
 Prints ONE JSON line.  `value` is whole-job tokens/s of the fwd+bwd step with
-inputs already resident in HBM.  `roofline` reports the dominant kernel of the
-step against the HBM roofline; `roofline_fwd` reports the fused forward on its
-own (inference call, no state save).  `cpu_baseline` times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+inputs already resident in HBM.  `roofline` reports the step's dominant kernel
+against the HBM roofline, timed with HIP events on the stream the library
+launches on; `roofline_fwd` reports the fused forward on its own (inference
+call, no state save).  `cpu_baseline` times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
 
-Algorithmic bytes (inputs read once, outputs written once; anything the
-implementation saves or recomputes is not counted):
-  forward  per token-head: q, k, g (dk bf16 each) + v (dv bf16) + beta (bf16)
-           + o (dv fp32); per (sequence, head): initial + final state (fp32)
-  backward per token-head: q, k, g, v, beta, dO (bf16) + dq, dk, dg, dv, dbeta
-           (fp32); per (sequence, head): initial state, dS_final, d(initial state)
+Algorithmic bytes (inputs read once, outputs written once; what the
+implementation saves or recomputes is not counted), per kernel:
+  forward         per token-head: q, k, g (dk bf16 each) + v (dv bf16) + beta
+                  (bf16) + o (dv fp32); per (sequence, head): initial + final state
+  chunk gradients per token-head: q, k, g, v, beta, dO (bf16) + dq, dk, dg, dv,
+                  dbeta (fp32)
+  state scan      per (sequence, head): dS_final in, d(initial state) out
 """
 import argparse
 import json
@@ -32,11 +35,32 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-def alg_bytes(B, T, H, dk, dv, mode):
+def alg_bytes(B, T, H, dk, dv, kernel):
     th = B * T * H
-    fwd = th * (3 * dk * 2 + dv * 2 + 2 + dv * 4) + B * H * 2 * dk * dv * 4
-    bwd = th * (3 * dk * 2 + dv * 2 + 2 + dv * 2) + th * (3 * dk * 4 + dv * 4 + 4) + B * H * 3 * dk * dv * 4
-    return {"fwd": fwd, "bwd": bwd, "fwdbwd": fwd + bwd}[mode]
+    state = dk * dv * 4
+    return {
+        "fwd": th * (3 * dk * 2 + dv * 2 + 2 + dv * 4) + B * H * 2 * state,
+        "grads": th * (3 * dk * 2 + dv * 2 + 2 + dv * 2) + th * (3 * dk * 4 + dv * 4 + 4),
+        "scan": B * H * 2 * state,
+    }[kernel]
+
+
+def traffic_record(kernel):
+    """Counter-measured HBM bytes per launch of `kernel`, from the committed
+    rocprofv3 summary (profiles/traffic.json), if it was taken on the current
+    source of that kernel; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(x, cu, spec, heads):
@@ -96,16 +120,19 @@ def main():
     def fwd_train():
         return kda.kda_fwd(q, k, v, g, b, cu_t, s0, save_for_bwd=True)
 
-    def bwd(saved):
-        return kda.kda_bwd(q, k, v, g, b, saved, dO, cu_t, s0, dS)
+    def bwd(saved, stage="all", out=None):
+        return kda.kda_bwd(q, k, v, g, b, saved, dO, cu_t, s0, dS, stage=stage, out=out)
 
     for _ in range(args.warmup):
         _, _, saved = fwd_train()
         bwd(saved)
     torch.cuda.synchronize()
+    _, _, saved = fwd_train()
+    out = bwd(saved)          # outputs and workspace, reused by every timed step
+    torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)   # the library launches on this stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_wall0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -114,14 +141,16 @@ def main():
         ev[i][0].record(stream)
         _, _, saved = fwd_train()
         ev[i][1].record(stream)
-        bwd(saved)
+        bwd(saved, "scan", out)
         ev[i][2].record(stream)
+        bwd(saved, "grads", out)
+        ev[i][3].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     ms_step = start.elapsed_time(end) / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    kms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+           for j, name in enumerate(("fwd", "scan", "grads"))}
 
     # the inference forward on its own (no state save): the fused forward kernel alone
     n_inf = max(5, args.steps)
@@ -136,15 +165,15 @@ def main():
     inf_ms = e0.elapsed_time(e1) / n_inf
 
     tokens = B * T
-    fb_bytes = alg_bytes(B, T, H, dk, dv, "fwdbwd")
+    names = {"fwd": "kda_fwd_bf16_kernel (training forward, state save)",
+             "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
+             "grads": "kda_bwd_chunk_kernel (chunk-parallel gradients)"}
+    dom = max(kms, key=kms.get)
+    dbytes = alg_bytes(B, T, H, dk, dv, dom)
+    ach = dbytes / (kms[dom] * 1e-3) / 1e9
+    traffic = traffic_record(dom)
     f_bytes = alg_bytes(B, T, H, dk, dv, "fwd")
-    b_bytes = alg_bytes(B, T, H, dk, dv, "bwd")
-    # dominant kernel launch of the step: the backward call (two kernels) or the forward call
-    if bwd_ms >= fwd_ms:
-        dom = {"kernel": "kda_bwd (state scan + chunk gradients)", "ms": bwd_ms, "bytes": b_bytes}
-    else:
-        dom = {"kernel": "kda_fwd_kernel (training, state save)", "ms": fwd_ms, "bytes": f_bytes}
-    ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    step_bytes = sum(alg_bytes(B, T, H, dk, dv, kname) for kname in kms)
     line = {
         "metric": "KDA fwd+bwd tokens/s (H=32, d=128, T=8192)",
         "value": tokens / (ms_step * 1e-3),
@@ -160,16 +189,17 @@ def main():
         "data": "synthetic (seeded, kda_inputs workload 2)",
         "config": {"workload": spec["name"], "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
                    "global_batch": B, "seq_len": T, "state": "fp32", "outputs": "fp32"},
-        "fwd_ms": fwd_ms,
-        "bwd_ms": bwd_ms,
+        "kernel_ms": kms,
         "fwd_infer_ms": inf_ms,
         "fwd_infer_tokens_per_s": tokens / (inf_ms * 1e-3),
-        "step_hbm_frac": fb_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": ach, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None},
-        "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd_kernel (inference, no save)",
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": traffic, "alg_bytes_per_launch": dbytes, "ms_per_launch": kms[dom]},
+        "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd_bf16_kernel (inference, no save)",
                          "achieved": f_bytes / (inf_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None},
+                         "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes},
         "timed_wall_s": wall,
     }
     if args.cpu_heads > 0:

@@ -104,9 +104,15 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: 
 
 def kda_bwd(q, k, v, g, beta, saved, dO, cu_seqlens=None, initial_state=None, dS_final=None, *,
             num_seqs: Optional[int] = None, out_dtype=None, eps: float = 1e-6, scale: float = 1.0,
-            output_d_initial_state: bool = True):
+            output_d_initial_state: bool = True, stage: str = "all", out=None):
     """KDA backward for the loss <dO, o> + <dS_final, final_state>.  Returns a
-    dict with dq, dk, dv, dg, dbeta and dS0 (None unless requested)."""
+    dict with dq, dk, dv, dg, dbeta, dS0 (None unless requested) and the
+    workspace.
+
+    stage "all" calls kda_bwd; "scan" and "grads" call its two stages
+    (kda_bwd_scan, kda_bwd_grads).  Pass the dict returned by the "scan" call as
+    `out` to the "grads" call: it carries the outputs and the workspace the
+    second stage reads."""
     torch = _torch()
     T, H, dk, dv, N, dev, dt = _common(q, k, v, g, beta, cu_seqlens, num_seqs)
     out_dtype = out_dtype or torch.float32
@@ -117,20 +123,26 @@ def kda_bwd(q, k, v, g, beta, saved, dO, cu_seqlens=None, initial_state=None, dS
     need = kda_saved_size(cfg, T, N)
     if saved is None or saved.dtype != torch.uint8 or saved.numel() < need or saved.device != dev:
         raise ValueError(f"saved must be a uint8 device tensor of at least {need} bytes from kda_fwd(save_for_bwd=True)")
-    out = {
-        "dq": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
-        "dk": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
-        "dv": torch.empty((T, H, dv), dtype=out_dtype, device=dev),
-        "dg": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
-        "dbeta": torch.empty((T, H), dtype=out_dtype, device=dev),
-        "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_d_initial_state else None,
-    }
+    if stage not in _lib.BWD_ENTRY:
+        raise ValueError(f"stage must be one of {sorted(_lib.BWD_ENTRY)}")
     wsb = kda_bwd_workspace_size(cfg, T, N)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {
+            "dq": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+            "dk": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+            "dv": torch.empty((T, H, dv), dtype=out_dtype, device=dev),
+            "dg": torch.empty((T, H, dk), dtype=out_dtype, device=dev),
+            "dbeta": torch.empty((T, H), dtype=out_dtype, device=dev),
+            "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_d_initial_state else None,
+            "workspace": torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev),
+        }
+    ws = out["workspace"]
+    if ws.numel() < wsb:
+        raise ValueError(f"workspace must hold at least {wsb} bytes")
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.kda_bwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                     _ptr(initial_state), _ptr(saved), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
-                                    _ptr(out["dS0"]), _ptr(ws), wsb, stream))
+                                    _ptr(out["dS0"]), _ptr(ws), wsb, stream, stage))
     return out

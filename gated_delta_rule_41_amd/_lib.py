@@ -68,8 +68,10 @@ def load():
         fn.restype = ctypes.c_size_t
     lib.kda_fwd.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 11 + [ctypes.c_size_t, _vp]
     lib.kda_fwd.restype = ctypes.c_int
-    lib.kda_bwd.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 17 + [ctypes.c_size_t, _vp]
-    lib.kda_bwd.restype = ctypes.c_int
+    for name in ("kda_bwd", "kda_bwd_scan", "kda_bwd_grads"):
+        fn = getattr(lib, name)
+        fn.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 17 + [ctypes.c_size_t, _vp]
+        fn.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -113,10 +115,14 @@ def kda_fwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initi
                           initial_state, o, final_state, saved, workspace, workspace_bytes, stream)
 
 
+BWD_ENTRY = {"all": "kda_bwd", "scan": "kda_bwd_scan", "grads": "kda_bwd_grads"}
+
+
 def kda_bwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved,
                 dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes,
-                stream) -> int:
-    """Direct call of kda_bwd with integer device addresses (0 = NULL); returns the status."""
-    return load().kda_bwd(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens,
-                          initial_state, saved, dO, dS_final, dq, dk, dv, dg, dbeta,
-                          d_initial_state, workspace, workspace_bytes, stream)
+                stream, stage: str = "all") -> int:
+    """Direct call of kda_bwd (stage "all"), kda_bwd_scan ("scan") or kda_bwd_grads
+    ("grads") with integer device addresses (0 = NULL); returns the status."""
+    fn = getattr(load(), BWD_ENTRY[stage])
+    return fn(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved,
+              dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream)

@@ -179,11 +179,11 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     return KDA_OK;
 }
 
-kda_status kda_bwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
-                   const void* v, const void* g, const void* beta, const int32_t* cu,
-                   const float* s0, const void* saved, const void* dO, const float* dSf, void* dq,
-                   void* dk, void* dv, void* dg, void* dbeta, float* dS0, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t N, const void* q,
+                           const void* k, const void* v, const void* g, const void* beta, const int32_t* cu,
+                           const float* s0, const void* saved, const void* dO, const float* dSf, void* dq,
+                           void* dk, void* dv, void* dg, void* dbeta, float* dS0, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     KDA_TRY(check_config(cfg));
     KDA_TRY(check_sizes(cfg, T, N, cu));
@@ -229,10 +229,22 @@ kda_status kda_bwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     p.eps = cfg->l2_eps; p.scale = cfg->scale;
     p.nslices = cfg->dv / kda::kSlice;
     (void)s0;
-    hipError_t e = kda::launch_bwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, (hipStream_t)stream);
+    hipError_t e = kda::launch_bwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, stages, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }
+
+#define KDA_BWD_ARGS                                                                                   \
+    const kda_config *cfg, int64_t T, int32_t N, const void *q, const void *k, const void *v, const void *g, \
+        const void *beta, const int32_t *cu, const float *s0, const void *saved, const void *dO,          \
+        const float *dSf, void *dq, void *dk, void *dv, void *dg, void *dbeta, float *dS0, void *workspace, \
+        size_t workspace_bytes, void *stream
+#define KDA_BWD_PASS cfg, T, N, q, k, v, g, beta, cu, s0, saved, dO, dSf, dq, dk, dv, dg, dbeta, dS0, workspace, \
+                     workspace_bytes, stream
+
+kda_status kda_bwd(KDA_BWD_ARGS) { return bwd_call(kda::kBwdScan | kda::kBwdGrads, KDA_BWD_PASS); }
+kda_status kda_bwd_scan(KDA_BWD_ARGS) { return bwd_call(kda::kBwdScan, KDA_BWD_PASS); }
+kda_status kda_bwd_grads(KDA_BWD_ARGS) { return bwd_call(kda::kBwdGrads, KDA_BWD_PASS); }
 
 const char* kda_status_string(kda_status s) {
     switch (s) {

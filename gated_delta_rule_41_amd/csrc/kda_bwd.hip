@@ -2134,19 +2134,23 @@ static hipError_t launch_chunk(const BwdParams& p, hipStream_t s) {
 }
 
 template <typename T, typename TO, int DK>
-static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-    hipError_t e = launch_scan<T, DK>(p, s);
-    if (e != hipSuccess) return e;
-    return launch_chunk<T, TO, DK>(p, s);
+static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t s) {
+    if (stages & kBwdScan) {
+        const hipError_t e = launch_scan<T, DK>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    if (stages & kBwdGrads) return launch_chunk<T, TO, DK>(p, s);
+    return hipSuccess;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, int stages, hipStream_t s) {
     if (in_dtype == 1) {
         if (dk == 128)
-            return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 128>(p, s) : launch_bwd_t<bf16, float, 128>(p, s);
-        return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 64>(p, s) : launch_bwd_t<bf16, float, 64>(p, s);
+            return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 128>(p, stages, s)
+                                  : launch_bwd_t<bf16, float, 128>(p, stages, s);
+        return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 64>(p, stages, s) : launch_bwd_t<bf16, float, 64>(p, stages, s);
     }
-    return out_dtype == 1 ? launch_bwd_t<float, bf16, 64>(p, s) : launch_bwd_t<float, float, 64>(p, s);
+    return out_dtype == 1 ? launch_bwd_t<float, bf16, 64>(p, stages, s) : launch_bwd_t<float, float, 64>(p, stages, s);
 }
 
 }  // namespace kda

@@ -74,6 +74,8 @@ struct BwdParams {
 // in_dtype / out_dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save,
                       hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, hipStream_t stream);
+// Backward stages (bit mask): the reverse state scan, then the chunk-parallel gradients.
+constexpr int kBwdScan = 1, kBwdGrads = 2;
+hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, int stages, hipStream_t stream);
 
 }  // namespace kda

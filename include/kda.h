@@ -130,6 +130,30 @@ kda_status kda_bwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs
                    void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* The two stages of kda_bwd, for callers that schedule or time them apart:
+ * kda_bwd_scan runs the reverse state-gradient scan (it writes d_initial_state
+ * and fills the workspace with dL/dS at the end of every chunk and, for bf16
+ * inputs, each chunk's dL/dU); kda_bwd_grads runs the chunk-parallel gradients
+ * from that workspace (it writes dq, dk, dv, dg, dbeta).  Both take exactly
+ * kda_bwd's arguments and check them the same way.  kda_bwd_scan followed by
+ * kda_bwd_grads on one stream, with the same arguments and the same workspace,
+ * equals kda_bwd; the workspace must not be changed in between.  (Stage split:
+ * "state-gradient propagation" and the Q/K gradients of "TorchTitan Ascend
+ * open source: Kimi K3.1 Pro adaptation and training practice", section
+ * "KDA pre/post-processing fusion".) */
+kda_status kda_bwd_scan(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
+                        const void* k, const void* v, const void* g, const void* beta,
+                        const int32_t* cu_seqlens, const float* initial_state, const void* saved,
+                        const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                        void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream);
+kda_status kda_bwd_grads(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
+                         const void* k, const void* v, const void* g, const void* beta,
+                         const int32_t* cu_seqlens, const float* initial_state, const void* saved,
+                         const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                         void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Static description of a status code. */
 const char* kda_status_string(kda_status s);
 /* Thread-local description of the last failure on this thread ("" if none). */

@@ -83,7 +83,7 @@ def test_bwd_w0_shape_fp32():
 
 
 def test_bwd_deterministic_and_adjoint():
-    """Bitwise-repeatable backward; and the adjoint identity
+    """Bitwise-repeatable backward (also when run as its two stages); and the adjoint identity
     <dv, v> + <dS0, S0> = <dO, o> + <dS_final, S_T> (o and S_T are linear in v, S0)."""
     need_gpu()
     _say("bwd determinism / adjoint identity")
@@ -91,8 +91,15 @@ def test_bwd_deterministic_and_adjoint():
     gr, (o, sf, saved, d, s0, dS, _) = _run(x, "bf16", num_seqs=2)
     gr2 = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], None, s0, dS, num_seqs=2)
     torch.cuda.synchronize()
-    for k in gr:
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
         assert torch.equal(gr[k], gr2[k]), k
+    # the two stages, called in order with one workspace, equal kda_bwd bitwise
+    st = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], None, s0, dS, num_seqs=2, stage="scan")
+    st = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], None, s0, dS, num_seqs=2, stage="grads",
+                     out=st)
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        assert torch.equal(gr[k], st[k]), ("stages", k)
     lhs = float((host(gr["dv"]) * x["v"]).sum() + (host(gr["dS0"]) * x["s0"]).sum())
     rhs = float((host(o) * x["dO"]).sum() + (host(sf) * x["dS"]).sum())
     _say(f"adjoint lhs={lhs:.6e} rhs={rhs:.6e}")
