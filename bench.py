@@ -63,6 +63,67 @@ def traffic_record(kernel):
     return rec["bytes_per_launch"]
 
 
+KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file)
+    "grads": ("kda_bwd_chunk_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
+    "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
+    "fwd": ("kda_fwd_bf16_kernel<float, 128, true>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
+    "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
+}
+
+
+def pmc_summary(fetch_csv, write_csv, probe_mib):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench kernels, each
+    scaled by the same counter's reading for the copy probe (the run's last
+    dispatch), whose true traffic is known: probe_mib MiB read and as many
+    written.  Writes profiles/traffic.json (keyed to the kernels' source
+    hashes) and prints a markdown summary."""
+    import csv
+    import hashlib
+
+    def per_dispatch(path, counter):
+        sums = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                    sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+        return sums
+
+    probe_bytes = probe_mib * (1 << 20)
+    rec, scale = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        sums = per_dispatch(path, counter)
+        last = max(sums)
+        scale[counter] = probe_bytes / (sums[last] * 1024.0)
+        rec.setdefault("_probe", {"bytes_read": probe_bytes, "bytes_written": probe_bytes})[counter] = {
+            "kernel": last[1][:100], "kib": sums[last], "scale": scale[counter]}
+        for key, (needle, src) in KERNELS.items():
+            vals = [v for (_, name), v in sums.items() if needle in name]
+            if vals:
+                rec.setdefault(key, {"kernel": needle, "source": src, "dispatches": len(vals)})[counter + "_kib"] = \
+                    sum(vals) / len(vals)
+    for key, r in rec.items():
+        if key.startswith("_") or "FETCH_SIZE_kib" not in r or "WRITE_SIZE_kib" not in r:
+            continue
+        r["fetch_bytes"] = r["FETCH_SIZE_kib"] * 1024.0 * scale["FETCH_SIZE"]
+        r["write_bytes"] = r["WRITE_SIZE_kib"] * 1024.0 * scale["WRITE_SIZE"]
+        r["bytes_per_launch"] = r["fetch_bytes"] + r["write_bytes"]
+        with open(os.path.join(ROOT, r["source"]), "rb") as f:
+            r["source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |")
+    print("|---|---|---|---|")
+    for key, r in rec.items():
+        if "bytes_per_launch" in r:
+            print(f"| {r['kernel']} | {r['FETCH_SIZE_kib']:.0f} | {r['WRITE_SIZE_kib']:.0f} | {r['bytes_per_launch']:.4g} |")
+    p = rec["_probe"]
+    print(f"\ncopy probe ({p['FETCH_SIZE']['kernel']}): {probe_mib} MiB read + written; FETCH_SIZE "
+          f"{p['FETCH_SIZE']['kib']:.0f} KiB (scale {p['FETCH_SIZE']['scale']:.4f}), WRITE_SIZE "
+          f"{p['WRITE_SIZE']['kib']:.0f} KiB (scale {p['WRITE_SIZE']['scale']:.4f})")
+
+
 def cpu_baseline(x, cu, spec, heads):
     """fp64 oracle, forward + backward, on the first sequence and `heads` heads."""
     import numpy as np
@@ -91,7 +152,18 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's CPU sample (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed run, one plain device copy of this many MiB (the reference "
+                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE counter files of "
+                         "a run with --copy-probe-mib into profiles/traffic.json and print a summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        if args.copy_probe_mib <= 0:
+            ap.error("--pmc-summary needs the --copy-probe-mib value of the profiled run")
+        pmc_summary(*args.pmc_summary, args.copy_probe_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
@@ -202,6 +274,14 @@ def main():
                          "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes},
         "timed_wall_s": wall,
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = 2 * n * 4
     if args.cpu_heads > 0:
         line["cpu_baseline"] = cpu_baseline(x, cu, spec, args.cpu_heads)
     print(json.dumps(line), flush=True)
