@@ -64,7 +64,7 @@ def traffic_record(kernel):
 
 
 KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file)
-    "grads": ("kda_bwd_chunk_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
+    "grads": ("kda_bwd_grads_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
     "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
     "fwd": ("kda_fwd_bf16_kernel<float, 128, true>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
     "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
@@ -239,7 +239,7 @@ def main():
     tokens = B * T
     names = {"fwd": "kda_fwd_bf16_kernel (training forward, state save)",
              "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
-             "grads": "kda_bwd_chunk_kernel (chunk-parallel gradients)"}
+             "grads": "kda_bwd_grads_kernel (chunk-parallel gradients)"}
     dom = max(kms, key=kms.get)
     dbytes = alg_bytes(B, T, H, dk, dv, dom)
     ach = dbytes / (kms[dom] * 1e-3) / 1e9

@@ -5,15 +5,17 @@
 // gradients ("TorchTitan Ascend open source: Kimi K3.1 Pro adaptation and
 // training practice", section "KDA pre/post-processing fusion").  Here:
 //
-//  B1  kda_bwd_scan_kernel: reverse state-gradient scan.  One persistent
-//      workgroup per (sequence, head, 64-column value slice) walks the chunks
-//      backwards with dL/dS (dk x 64, fp32) resident in MFMA accumulators:
+//  B1  reverse state-gradient scan (kda_bwd_scan_bf16_kernel; kda_bwd_scan_kernel
+//      for fp32 inputs).  One persistent workgroup per (sequence, head,
+//      64-column value slice) walks the chunks backwards with dL/dS (dk x 64,
+//      fp32) resident in MFMA accumulators:
 //          dU  = Aqk^T dO + Ktil dS1
 //          dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
-//      and writes dS1 (dL/dS at the end of every chunk) for B2.
-//  B2  kda_bwd_chunk_kernel: chunk-parallel gradients.  One workgroup per
-//      (chunk, head) recomputes the chunk's intra matrices, reads the saved
-//      entering state S0 and dS1, and forms dq, dk, dv, dg, dbeta.
+//      and writes dS1 (dL/dS at the end of every chunk) and dU for B2.
+//  B2  chunk-parallel gradients (kda_bwd_grads_kernel; kda_bwd_chunk_f32_kernel
+//      for fp32 inputs).  One workgroup per (chunk, head) recomputes the
+//      chunk's Akk and T, reads the saved entering state S0, U, dS1 and dU, and
+//      forms dq, dk, dv, dg, dbeta.
 //
 // Chunk equations (G the in-chunk cumulative log-decay, Gam = exp(G)):
 //   QG = qh Gam, KG = beta kh Gam, KI = kh / Gam, Ktil = kh Gam_C / Gam
@@ -894,7 +896,10 @@ __device__ __forceinline__ void put_blk_tp(T* hi, T* lo, int ld, int m0, int n0,
 // N contiguous outputs from fp32 values, as 16-byte stores.
 template <typename TO, int N>
 __device__ __forceinline__ void store_row(TO* p, const float (&v)[N]) {
-    if constexpr (sizeof(TO) == 4) {
+    if constexpr (N % 4 != 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) p[j] = from_f32<TO>(v[j]);
+    } else if constexpr (sizeof(TO) == 4) {
 #pragma unroll
         for (int j = 0; j < N; j += 4) *reinterpret_cast<f32x4*>(p + j) = f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]};
     } else {
@@ -904,16 +909,26 @@ __device__ __forceinline__ void store_row(TO* p, const float (&v)[N]) {
     }
 }
 
-template <typename T, typename TO, int DK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p) {
+// ============================================================================
+// B2 for bf16 inputs with 8 waves.
+//
+// Laid out for two waves per SIMD: every dk- or dv-wide output (64 rows x 16
+// columns per block) belongs to wave w for column block w; the 64x64 products
+// (Akk, T, dAqk, dT, dAkk) run on waves 0-3; the prep layout (q/k/g rows, the
+// tiles written from them, the chain rule) gives wave w rows
+// 16(w&3)..16(w&3)+15 and one half of the key columns, the two halves' row sums
+// meeting in LDS.
+// ============================================================================
+template <typename TO, int DK, int DV>
+__global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParams p) {
+    typedef bf16 T;
     typedef ChunkLds<T, DK, DV> LY;
     __shared__ __attribute__((aligned(256))) char lds[LY::BYTES];
-    constexpr bool SPLIT = std::is_same<T, bf16>::value;
+    constexpr bool SPLIT = true;
     constexpr int PK = LY::PK, PV = LY::PV, PC = LY::PC, PF = LY::PF;
-    constexpr int CPL = DK / 16, VPL = DV / 16;
-    constexpr int NBK = DK / 64, NBV = DV / 64;     // column blocks per wave (dk- / dv-wide outputs)
-    constexpr int NKK = DK / 32, NKV = DV / 32;     // k32 steps over dk / dv
-    typedef typename V8<T>::t V8T;
+    constexpr int CPH = DK / 32, VPH = DV / 32;   // key / value columns per lane (prep layout, half a row)
+    constexpr int NKK = DK / 32, NKV = DV / 32;   // k32 steps over dk / dv
+    typedef bf16x8 V8T;
     auto S = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT); };
     auto Sh = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT + LY::RQ); };   // second half
     auto Sf = [&](int i) { return reinterpret_cast<float*>(lds + i * LY::SLOT); };
@@ -923,8 +938,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     float* const sdgc = reinterpret_cast<float*>(lds + LY::DGC);
     float* const sred = reinterpret_cast<float*>(lds + LY::RED);
     float* const sdbv = reinterpret_cast<float*>(lds + LY::DBV);
+    float* const sgw = reinterpret_cast<float*>(lds + LY::GW);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const int wl = w & 3, wh = w >> 2;
+    const bool kact = w < DK / 16, vact = w < DV / 16;   // owns key / value column block 16w
     const int H = p.H;
     const int64_t slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -947,25 +965,28 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // ================= prep (rows 16w+4qg+i, key cols CPL*cl+e) =================
-    // The raw rows and gate cumsums are not kept across the kernel (they would
-    // spill): prep_fill reloads them (L2-resident) and rebuilds G from the
-    // per-wave column sums of g, which the first call leaves in LDS.
-    float* const sgw = reinterpret_cast<float*>(lds + LY::GW);
+    const int r0 = 16 * wl + 4 * qg;             // prep layout: rows r0..r0+3
+    const int ck0 = wh * (DK / 2) + CPH * cl;    //   key columns ck0..ck0+CPH-1
+    const int cv0 = wh * (DV / 2) + VPH * cl;    //   value columns cv0..cv0+VPH-1
+
+    // ================= prep =================
+    // The raw rows and gate cumsums are not kept across the kernel: prep_fill
+    // reloads them (L2-resident) and rebuilds G from the per-wave column sums of
+    // g, which the first call leaves in LDS.
     struct Prep {
-        RawRow<T, CPL> q[4], k[4];
-        float G[4][CPL], GC[CPL], beta[4], iq[4], ik[4];
+        RawRow<T, CPH> q[4], k[4];
+        float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4];
     };
     auto prep_fill = [&](Prep& P, bool first) {
-        RawRow<T, CPL> rg[4];
+        RawRow<T, CPH> rg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * qg + i;
+            const int r = r0 + i;
             float rb = 0.f, nq = 1.f, nk = 1.f;
             if (r < L) {
-                P.q[i].load(qc + r * rsk + CPL * cl);
-                P.k[i].load(kc + r * rsk + CPL * cl);
-                rg[i].load(gcp + r * rsk + CPL * cl);
+                P.q[i].load(qc + r * rsk + ck0);
+                P.k[i].load(kc + r * rsk + ck0);
+                rg[i].load(gcp + r * rsk + ck0);
                 rb = gload1(bc + (int64_t)r * H);
                 nq = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
                 nk = p.nk_saved[(c0 + r) * H + h];
@@ -977,7 +998,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             P.ik[i] = 1.f / nk;
         }
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
+        for (int e = 0; e < CPH; ++e) {
             float a = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) { a += rg[i][e] * kLog2e; P.G[i][e] = a; }
@@ -990,17 +1011,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             const float excl = s - tot;
 #pragma unroll
             for (int i = 0; i < 4; ++i) P.G[i][e] += excl;
-            if (first && qg == 3) sgw[w * DK + CPL * cl + e] = s;
+            if (first && qg == 3) sgw[wl * DK + ck0 + e] = s;
         }
         if (first) lds_barrier();
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int c = CPL * cl + e;
+        for (int e = 0; e < CPH; ++e) {
+            const int c = ck0 + e;
             float a = 0.f, tot = 0.f;
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {
                 const float x = sgw[w2 * DK + c];
-                if (w2 < w) a += x;
+                if (w2 < wl) a += x;
                 tot += x;
             }
 #pragma unroll
@@ -1008,72 +1029,72 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             P.GC[e] = tot;
         }
     };
-    // prep-layout value of qh*Gam, beta*kh*Gam, kh/Gam, Ktil at (row i, col e)
+    // prep-layout value of qh*Gam, beta*kh*Gam, kh/Gam at (row i, col e)
     auto vQG = [&](const Prep& P, int i, int e) { return P.q[i][e] * P.iq[i] * fast_exp2(P.G[i][e]); };
     auto vKG = [&](const Prep& P, int i, int e) { return P.k[i][e] * (P.beta[i] * P.ik[i]) * fast_exp2(P.G[i][e]); };
     auto vKI = [&](const Prep& P, int i, int e) { return P.k[i][e] * P.ik[i] * fast_exp2(-P.G[i][e]); };
-    auto vKt = [&](const Prep& P, int i, int e) { return P.k[i][e] * P.ik[i] * fast_exp2(P.GC[e] - P.G[i][e]); };
-    // writers: row-major [r][c] tile (stride PK) or transposed [c][perm32(r)] tile (stride PC)
+    // writers: row-major [r][c] tile (stride PK) or transposed [c][r] tile (stride PC)
     auto put_rm = [&](const Prep& P, T* hi, T* lo, auto val, bool split) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * qg + i;
-#pragma unroll
-            for (int e4 = 0; e4 < CPL; e4 += 4) {
-                f32x4 x;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = val(P, i, e4 + j);
-                const int o = r * PK + CPL * cl + e4;
-                if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
+            const int o = (r0 + i) * PK + ck0;
+            if constexpr (CPH == 4) {
+                const f32x4 x = {val(P, i, 0), val(P, i, 1), val(P, i, 2), val(P, i, 3)};
+                if (split) sts4_split<T, true>(hi + o, lo + o, x);
                 else sts4<T>(hi + o, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < CPH; ++e) {
+                    const float x = val(P, i, e);
+                    const T hv = from_f32<T>(x);
+                    hi[o + e] = hv;
+                    if (split) lo[o + e] = from_f32<T>(x - to_f32(hv));
+                }
             }
         }
     };
-    auto put_tp = [&](const Prep& P, T* hi, T* lo, auto val, bool split, bool perm) {
-        const int r0 = 16 * w + 4 * qg;
-        const int pr = perm ? perm32(r0) : r0;
+    auto put_tp = [&](const Prep& P, T* hi, T* lo, auto val, bool split) {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            f32x4 x = {val(P, 0, e), val(P, 1, e), val(P, 2, e), val(P, 3, e)};
-            const int o = (CPL * cl + e) * PC + pr;
-            if (SPLIT && split) sts4_split<T, true>(hi + o, lo + o, x);
+        for (int e = 0; e < CPH; ++e) {
+            const f32x4 x = {val(P, 0, e), val(P, 1, e), val(P, 2, e), val(P, 3, e)};
+            const int o = (ck0 + e) * PC + r0;
+            if (split) sts4_split<T, true>(hi + o, lo + o, x);
             else sts4<T>(hi + o, x);
         }
     };
-    // U (saved by the forward) and dU (left by the reverse scan) of this chunk,
-    // in accumulator layout: rows 16mb+4qg+i, value column 16(w+4t)+cl
-    f32x4 U[NBV][4], dU[NBV][4];
-    RawRow<T, VPL> ddr[4], vvr[4];   // dO and v rows of this lane, staged row-major in LDS later
+
+    // U (saved by the forward) and dU (left by the reverse scan) of this chunk for
+    // value column block 16w, accumulator layout: rows 16mb+4qg+i, column 16w+cl
+    f32x4 U[4], dU[4];
+    RawRow<T, VPH> ddr[4], vvr[4];   // dO and v rows of this lane (prep layout), staged in LDS later
     {
     Prep P;
     prep_fill(P, true);
-    {
+    if (vact) {
         const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
         const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
-        for (int t = 0; t < NBV; ++t)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * (w + 4 * t) + cl;
-                    U[t][mb][i] = ub[o];
-                    dU[t][mb][i] = dub[o];
-                }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * qg + i;
-            if (r < L) { vvr[i].load(vc + r * rsv + VPL * cl); ddr[i].load(doc + r * rsv + VPL * cl); }
-            else { vvr[i].zero(); ddr[i].zero(); }
-        }
+            for (int i = 0; i < 4; ++i) {
+                const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * w + cl;
+                U[mb][i] = ub[o];
+                dU[mb][i] = dub[o];
+            }
     }
-    if (w == 0 && qg == 0) {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) sgc[CPL * cl + e] = fast_exp2(P.GC[e]);
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        if (r < L) { vvr[i].load(vc + r * rsv + cv0); ddr[i].load(doc + r * rsv + cv0); }
+        else { vvr[i].zero(); ddr[i].zero(); }
     }
-    if (cl == 0) {
+    if (wl == 0 && qg == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sbeta[16 * w + 4 * qg + i] = P.beta[i];
+        for (int e = 0; e < CPH; ++e) sgc[ck0 + e] = fast_exp2(P.GC[e]);
+    }
+    if (wh == 0 && cl == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sbeta[r0 + i] = P.beta[i];
     }
     put_rm(P, S(2), S(2), vKI, false);   // KI  h
     put_rm(P, S(4), S(4), vKG, false);   // KG  h
@@ -1081,7 +1102,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 
     // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
-    {
+    if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -1101,26 +1122,24 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     lds_barrier();
     // ================= T = (I + Akk)^{-1} (fp32 in slot 7) =================
     float* const Tf = Sf(7);
-    {
+    for (int e = tid; e < kChunk * PF; e += kWideThreads) {
+        const int r = e / PF, c = e % PF;
+        if ((r >> 4) != (c >> 4) || c >= kChunk) Tf[e] = 0.f;
+    }
+    if (w < 4) {
         const f32x4 na = *reinterpret_cast<const f32x4*>(&Af[(16 * w + cl) * PF + 16 * w + 4 * qg]);
         f32x4 nbv;
 #pragma unroll
         for (int j = 0; j < 4; ++j) nbv[j] = Af[(16 * w + 4 * qg + j) * PF + 16 * w + cl];
         const f32x4 tw = inv_unit_lower16(na, nbv, qg, cl);
-        for (int e = tid; e < kChunk * PF; e += kThreads) {
-            const int r = e / PF, c = e % PF;
-            if ((r >> 4) != (c >> 4) || c >= kChunk) Tf[e] = 0.f;
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Tf[(16 * w + 4 * qg + i) * PF + 16 * w + cl] = tw[i];
     }
     lds_barrier();
     // off-diagonal blocks, column j on wave j: T_ij = -T_ii sum_{k=j}^{i-1} Akk_ik T_kj
-    // (fp32 MFMA; the column's blocks stay in accumulator layout, which is the
-    // B fragment of the next step)
     {
-        auto solve_col = [&](auto jc) {
-            constexpr int j = decltype(jc)::value;
+        auto solve_col = [&](auto jcst) {
+            constexpr int j = decltype(jcst)::value;
             f32x4 col[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) col[j][i] = Tf[(16 * j + 4 * qg + i) * PF + 16 * j + cl];
@@ -1145,61 +1164,70 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     {
         T* const Trm = S(5);
         T* const Ttp = S(0);
-        for (int e = tid; e < kChunk * kChunk; e += kThreads) {
+        for (int e = tid; e < kChunk * kChunk; e += kWideThreads) {
             const int r = e >> 6, c = e & 63;
             const float t = Tf[r * PF + c];
             Trm[r * PC + c] = from_f32<T>(t);
             Ttp[c * PC + perm32(r)] = from_f32<T>(t);
         }
-        put_tp(P, S(1), S(1), vKG, false, false);
+        put_tp(P, S(1), S(1), vKG, false);
     }
     }
     lds_barrier();
     // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6), v rm (slot 2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (16 * w + 4 * qg + i) * PV + VPL * cl) = ddr[i].x;
-        *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (16 * w + 4 * qg + i) * PV + VPL * cl) = vvr[i].x;
+        *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (r0 + i) * PV + cv0) = ddr[i].x;
+        *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (r0 + i) * PV + cv0) = vvr[i].x;
     }
-#pragma unroll
-    for (int t = 0; t < NBV; ++t)
+    if (vact) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * (w + 4 * t), U[t][mb], qg, cl, true);
-            put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * (w + 4 * t), dU[t][mb], qg, cl, true);
+            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * w, U[mb], qg, cl, true);
+            put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * w, dU[mb], qg, cl, true);
         }
+    }
     lds_barrier();
 
+    // S0 / dS1 row fragments of key column block 16w, issued before dBV and
+    // dAqk so their latency hides under those products
+    float xs0[NKV][8], xd0[NKV][8];
+    if (kact) {
+        const int nr = 16 * w + cl;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            gf8(xs0[kk], S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            gf8(xd0[kk], dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+        }
+    }
     // ================= dBV = T^T dU  ->  dv, dbeta (v part) =================
-    {
+    float dbv_part[4][4];   // this wave's share of sum_j v dBV per row (waves 4-7 add theirs later)
+    if (vact) {
         TO* __restrict__ dvp = reinterpret_cast<TO*>(p.dv_out) + c0 * rsv + h * DV;
         float rowpart[4][4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) rowpart[mb][i] = 0.f;
+        V8T bh[2], bl[2];
+        split8<T, SPLIT>(dU[0], dU[1], bh[0], bl[0]);
+        split8<T, SPLIT>(dU[2], dU[3], bh[1], bl[1]);
+        const int nc = 16 * w + cl;
 #pragma unroll
-        for (int t = 0; t < NBV; ++t) {
-            V8T bh[2], bl[2];
-            split8<T, SPLIT>(dU[t][0], dU[t][1], bh[0], bl[0]);
-            split8<T, SPLIT>(dU[t][2], dU[t][3], bh[1], bl[1]);
-            const int nc = 16 * (w + 4 * t) + cl;
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 a = zero;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                f32x4 a = zero;
+            for (int kk = 0; kk < 2; ++kk) {
+                const V8T ah = lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
+                a = mma_k32(a, ah, bh[kk]);
+                a = mma_k32(a, ah, bl[kk]);
+            }
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const V8T ah = lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
-                    a = mma_k32(a, ah, bh[kk]);
-                    if constexpr (SPLIT) a = mma_k32(a, ah, bl[kk]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mb + 4 * qg + i;
-                    if (r < L) {
-                        dvp[r * rsv + nc] = from_f32<TO>(sbeta[r] * a[i]);
-                        rowpart[mb][i] += to_f32(S(2)[r * PV + nc]) * a[i];
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mb + 4 * qg + i;
+                if (r < L) {
+                    dvp[r * rsv + nc] = from_f32<TO>(sbeta[r] * a[i]);
+                    rowpart[mb][i] += to_f32(S(2)[r * PV + nc]) * a[i];
                 }
             }
         }
@@ -1208,25 +1236,26 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float s = row16_sum(rowpart[mb][i]);
-                if (cl == 0) sdbv[w * 64 + 16 * mb + 4 * qg + i] = s;
+                dbv_part[mb][i] = s;
+                if (w < 4 && cl == 0) sdbv[w * 64 + 16 * mb + 4 * qg + i] = s;
             }
     }
-    // ================= dAqk = lower(dO U^T);  dT = (dU v^T) diag(beta) =================
+    // ================= dAqk = lower(dO U^T);  dT = (dU v^T) diag(beta) (waves 0-3) =================
     f32x4 dAqk[4], dT[4];
-    {
+    if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) { dAqk[mb] = zero; dT[mb] = zero; }
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
             const int kb = (nb + cl) * PV + 32 * kk + 8 * qg;
-            const V8T uh = lds8<T>(S(4) + kb), ul = lds8<T>(S(3) + (SPLIT ? kb : 0));
+            const V8T uh = lds8<T>(S(4) + kb), ul = lds8<T>(S(3) + kb);
             const V8T vb = lds8<T>(S(2) + kb);   // rows past the chunk end are zero
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const V8T da = lds8<T>(S(6) + (16 * mb + cl) * PV + 32 * kk + 8 * qg);
                 dAqk[mb] = mma_k32(dAqk[mb], da, uh);
-                if constexpr (SPLIT) dAqk[mb] = mma_k32(dAqk[mb], da, ul);
+                dAqk[mb] = mma_k32(dAqk[mb], da, ul);
                 dT[mb] = mma_k32(dT[mb], lds8<T>(S(7) + (16 * mb + cl) * PV + 32 * kk + 8 * qg), vb);
             }
         }
@@ -1240,55 +1269,57 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
                 dT[mb][i] *= bs;
             }
     }
-    // ================= dQG = dO S0^T;  dW = -dU S0^T;  dKt = U dS1^T =================
-    f32x4 dQG[NBK][4], dW[NBK][4], dKt[NBK][4];
+    // ================= dQG = dO S0^T;  dW = -dU S0^T;  dKt = U dS1^T (key column block 16w) =================
+    f32x4 dQG[4], dW[4], dKt[4];
+    if (kact) {
+        const int nr = 16 * w + cl;   // key row of S0 / dS1 feeding this lane
 #pragma unroll
-    for (int t = 0; t < NBK; ++t) {
-        const int nr = 16 * (w + 4 * t) + cl;   // key row of S0 / dS1 feeding this lane
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) { dQG[t][mb] = zero; dW[t][mb] = zero; dKt[t][mb] = zero; }
+        for (int mb = 0; mb < 4; ++mb) { dQG[mb] = zero; dW[mb] = zero; dKt[mb] = zero; }
         float gpart = 0.f;   // this lane's share of dL/dGam_C[nr] = sum_j S0[nr][j] dS1[nr][j]
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
-            float xs[8], xd[8];
             V8T sh, sl, dh, dl;
-            gf8(xs, S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-            gf8(xd, dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) gpart += xs[j] * xd[j];
-            if constexpr (SPLIT) cvt8(xs, sh, sl); else cvt8(xs, sh);
-            if constexpr (SPLIT) cvt8(xd, dh, dl); else cvt8(xd, dh);
+            for (int j = 0; j < 8; ++j) gpart += xs0[kk][j] * xd0[kk][j];
+            cvt8(xs0[kk], sh, sl);
+            cvt8(xd0[kk], dh, dl);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int r = 16 * mb + cl;
                 const V8T da = lds8<T>(S(6) + r * PV + 32 * kk + 8 * qg);
-                dQG[t][mb] = mma_k32(dQG[t][mb], da, sh);
-                if constexpr (SPLIT) dQG[t][mb] = mma_k32(dQG[t][mb], da, sl);
+                dQG[mb] = mma_k32(dQG[mb], da, sh);
+                dQG[mb] = mma_k32(dQG[mb], da, sl);
                 const int ka = r * PV + 32 * kk + 8 * qg;
-                dW[t][mb] = mma_k32(dW[t][mb], lds8<T>(S(7) + ka), sh);
-                dKt[t][mb] = mma3<SPLIT>(dKt[t][mb], lds8<T>(S(4) + ka), lds8<T>(S(3) + (SPLIT ? ka : 0)), dh,
-                                         SPLIT ? dl : dh);
+                dW[mb] = mma_k32(dW[mb], lds8<T>(S(7) + ka), sh);
+                dKt[mb] = mma3<true>(dKt[mb], lds8<T>(S(4) + ka), lds8<T>(S(3) + ka), dh, dl);
             }
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) dW[t][mb] = -dW[t][mb];
+        for (int mb = 0; mb < 4; ++mb) dW[mb] = -dW[mb];
         gpart += __shfl_xor(gpart, 16);
         gpart += __shfl_xor(gpart, 32);
         if (qg == 0) sdgc[nr] = gpart;
     }
     lds_barrier();
+    // waves 4-7 add their dbeta (v part) row sums after waves 0-3 wrote theirs: fixed order
+    if (w >= 4 && vact && cl == 0) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sdbv[(w - 4) * 64 + 16 * mb + 4 * qg + i] += dbv_part[mb][i];
+    }
     {
     Prep P;
     prep_fill(P, false);
     // dW rm (slot 2), KG rm (slot 6)
+    if (kact) {
 #pragma unroll
-    for (int t = 0; t < NBK; ++t)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(2), S(2), PK, 16 * mb, 16 * (w + 4 * t), dW[t][mb], qg, cl, true);
+        for (int mb = 0; mb < 4; ++mb) put_blk<T, false>(S(2), S(2), PK, 16 * mb, 16 * w, dW[mb], qg, cl, true);
+    }
     put_rm(P, S(6), S(6), vKG, false);
     lds_barrier();
-    // ================= dT += dW KG^T;  X = T^T dT -> slot 0 (2nd half) =================
-    {
+    // ================= dT += dW KG^T;  X = T^T dT -> slot 0 (2nd half) (waves 0-3) =================
+    if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -1309,9 +1340,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
         }
     }
     lds_barrier();
-    // ================= dAkk = -strict(X T^T) =================
+    // ================= dAkk = -strict(X T^T) (waves 0-3) =================
     f32x4 dAkk[4];
-    {
+    if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -1332,7 +1363,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     // tiles for the last products:
     //   dAkk rm [r][s] (slot 0, 2nd half), dAkk^T [s][r] (QX), dAqk rm h/l (slot 3),
     //   dAqk^T h/l (slot 7), KI^T h/l [c][s] (slots 2, 6), QG^T h/l [c][r] (slots 4, 5)
-    {
+    if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -1341,37 +1372,35 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             put_blk<T, SPLIT>(S(3), Sh(3), PC, 16 * mb, nb, dAqk[mb], qg, cl, true);
             put_blk<T, SPLIT>(S(7), Sh(7), PC, 16 * mb, nb, dAqk[mb], qg, cl, false);
         }
-        put_tp(P, S(2), S(6), vKI, true, false);
-        put_tp(P, S(4), S(5), vQG, true, false);
     }
+    put_tp(P, S(2), S(6), vKI, true);
+    put_tp(P, S(4), S(5), vQG, true);
     }
     lds_barrier();
     // ================= dKG = T^T dW + dAkk KI;  dQG += dAqk KI;  dKI = dAkk^T KG + dAqk^T QG =================
-    f32x4 dKG[NBK][4], dKI[NBK][4];
-#pragma unroll
-    for (int t = 0; t < NBK; ++t) {
-        const int nb = 16 * (w + 4 * t);
-        V8T wh[2], wl[2];
-        split8<T, false>(dW[t][0], dW[t][1], wh[0], wl[0]);
-        split8<T, false>(dW[t][2], dW[t][3], wh[1], wl[1]);
+    f32x4 dKG[4], dKI[4];
+    if (kact) {
+        const int nb = 16 * w;
+        V8T whi[2], wlo[2];
+        split8<T, false>(dW[0], dW[1], whi[0], wlo[0]);
+        split8<T, false>(dW[2], dW[3], whi[1], wlo[1]);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            f32x4 a = zero, qq = dQG[t][mb], ki = zero;
+            f32x4 a = zero, qq = dQG[mb], ki = zero;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = (nb + cl) * PC + 32 * kk + 8 * qg;
-                a = mma_k32(a, lds8<T>(S(0) + ka), wh[kk]);                                  // T^T dW
+                a = mma_k32(a, lds8<T>(S(0) + ka), whi[kk]);                                 // T^T dW
                 const V8T kih = lds8<T>(S(2) + kb);
                 a = mma_k32(a, lds8<T>(Sh(0) + ka), kih);                                    // dAkk KI
-                qq = mma3<SPLIT>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + (SPLIT ? ka : 0)), kih,
-                                 lds8<T>(S(6) + (SPLIT ? kb : 0)));                          // dAqk KI
+                qq = mma3<true>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + ka), kih, lds8<T>(S(6) + kb));   // dAqk KI
                 ki = mma_k32(ki, lds8<T>(QX + ka), lds8<T>(S(1) + kb));                      // dAkk^T KG
-                ki = mma3<SPLIT>(ki, lds8<T>(S(7) + ka), lds8<T>(Sh(7) + (SPLIT ? ka : 0)), lds8<T>(S(4) + kb),
-                                 lds8<T>(S(5) + (SPLIT ? kb : 0)));                          // dAqk^T QG
+                ki = mma3<true>(ki, lds8<T>(S(7) + ka), lds8<T>(Sh(7) + ka), lds8<T>(S(4) + kb),
+                                lds8<T>(S(5) + kb));                                         // dAqk^T QG
             }
-            dKG[t][mb] = a;
-            dQG[t][mb] = qq;
-            dKI[t][mb] = ki;
+            dKG[mb] = a;
+            dQG[mb] = qq;
+            dKI[mb] = ki;
         }
     }
     lds_barrier();
@@ -1382,49 +1411,48 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     float* const F1 = Sf(2);   // slots 2-3
     float* const F2 = Sf(4);   // slots 4-5
     static_assert(kChunk * LDF * 4 <= 2 * LY::SLOT, "fp32 staging");
-    float gQ[4][CPL], gKG[4][CPL], gKI[4][CPL], gKt[4][CPL];
-#pragma unroll
-    for (int t = 0; t < NBK; ++t)
+    float gQ[4][CPH], gKG[4][CPH], gKI[4][CPH], gKt[4][CPH];
+    if (kact) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            const int nb = 16 * (w + 4 * t);
-            st_blk(F0, LDF, 16 * mb, nb, dQG[t][mb], qg, cl);
-            st_blk(F1, LDF, 16 * mb, nb, dKG[t][mb], qg, cl);
-            st_blk(F2, LDF, 16 * mb, nb, dKI[t][mb], qg, cl);
+            st_blk(F0, LDF, 16 * mb, 16 * w, dQG[mb], qg, cl);
+            st_blk(F1, LDF, 16 * mb, 16 * w, dKG[mb], qg, cl);
+            st_blk(F2, LDF, 16 * mb, 16 * w, dKI[mb], qg, cl);
         }
+    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int o = (16 * w + 4 * qg + i) * LDF + CPL * cl + e;
+        for (int e = 0; e < CPH; ++e) {
+            const int o = (r0 + i) * LDF + ck0 + e;
             gQ[i][e] = F0[o];
             gKG[i][e] = F1[o];
             gKI[i][e] = F2[o];
         }
     lds_barrier();
+    if (kact) {
 #pragma unroll
-    for (int t = 0; t < NBK; ++t)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) st_blk(F0, LDF, 16 * mb, 16 * (w + 4 * t), dKt[t][mb], qg, cl);
+        for (int mb = 0; mb < 4; ++mb) st_blk(F0, LDF, 16 * mb, 16 * w, dKt[mb], qg, cl);
+    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) gKt[i][e] = F0[(16 * w + 4 * qg + i) * LDF + CPL * cl + e];
+        for (int e = 0; e < CPH; ++e) gKt[i][e] = F0[(r0 + i) * LDF + ck0 + e];
 
     // ================= chain rule to qh, kh, beta, G =================
     Prep P;
     prep_fill(P, false);
-    float dqh[4][CPL], dkh[4][CPL], dG[4][CPL], dbk[4], colp[CPL];
+    float dqh[4][CPH], dkh[4][CPH], dG[4][CPH], dbk[4], colp[CPH];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) colp[e] = 0.f;
+    for (int e = 0; e < CPH; ++e) colp[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         dbk[i] = 0.f;
         const float aq = P.iq[i], ai = P.ik[i];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
+        for (int e = 0; e < CPH; ++e) {
             const float gam = fast_exp2(P.G[i][e]), gin = fast_exp2(-P.G[i][e]), ek = fast_exp2(P.GC[e] - P.G[i][e]);
             const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
             const float QG = qh * gam, KGv = P.beta[i] * kh * gam, KIv = kh * gin, Ktv = kh * ek;
@@ -1435,25 +1463,42 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             colp[e] += gKt[i][e] * Ktv;
         }
     }
+    lds_barrier();   // F0 reads done before it holds the row sums below
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
+    for (int e = 0; e < CPH; ++e) {
         float s = colp[e];
         s += __shfl_xor(s, 16);
         s += __shfl_xor(s, 32);
-        if (qg == 0) sred[w * DK + CPL * cl + e] = s;
+        if (qg == 0) sred[wl * DK + ck0 + e] = s;
+    }
+    // per-half row sums: qh . dqh, kh . dkh, and the k part of dbeta
+    float* const srow = F0;   // [2 halves][3][64]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPH; ++e) { sq += P.q[i][e] * P.iq[i] * dqh[i][e]; sk += P.k[i][e] * P.ik[i] * dkh[i][e]; }
+        sq = row16_sum(sq);
+        sk = row16_sum(sk);
+        const float db = row16_sum(dbk[i]);
+        if (cl == 0) {
+            srow[(wh * 3 + 0) * 64 + r0 + i] = sq;
+            srow[(wh * 3 + 1) * 64 + r0 + i] = sk;
+            srow[(wh * 3 + 2) * 64 + r0 + i] = db;
+        }
     }
     lds_barrier();
-    float dGC[CPL];
+    float dGC[CPH];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-        const int c = CPL * cl + e;
+    for (int e = 0; e < CPH; ++e) {
+        const int c = ck0 + e;
         dGC[e] = sred[c] + sred[DK + c] + sred[2 * DK + c] + sred[3 * DK + c] + sdgc[c] * sgc[c];
     }
     lds_barrier();
     {
-        float suf[CPL];
+        float suf[CPH];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
+        for (int e = 0; e < CPH; ++e) {
             float a = 0.f;
 #pragma unroll
             for (int i = 3; i >= 0; --i) { a += dG[i][e]; dG[i][e] = a; }
@@ -1464,16 +1509,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
             x = __shfl_down(s, 32);
             if (qg <= 1) s += x;
             suf[e] = s - tot;
-            if (qg == 0) sred[w * DK + CPL * cl + e] = s;
+            if (qg == 0) sred[wl * DK + ck0 + e] = s;
         }
         lds_barrier();
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int c = CPL * cl + e;
+        for (int e = 0; e < CPH; ++e) {
+            const int c = ck0 + e;
             float a = suf[e] + dGC[e];
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww)
-                if (ww > w) a += sred[ww * DK + c];
+            for (int w2 = 0; w2 < 4; ++w2)
+                if (w2 > wl) a += sred[w2 * DK + c];
 #pragma unroll
             for (int i = 0; i < 4; ++i) dG[i][e] += a;
         }
@@ -1485,29 +1530,26 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_kernel(BwdParams p)
     TO* __restrict__ dbp = reinterpret_cast<TO*>(p.db) + c0 * H + h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * qg + i;
-        const float aq = P.iq[i], ai = P.ik[i];
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) { sq += P.q[i][e] * aq * dqh[i][e]; sk += P.k[i][e] * ai * dkh[i][e]; }
-        sq = row16_sum(sq);
-        sk = row16_sum(sk);
-        const float db = row16_sum(dbk[i]);
+        const int r = r0 + i;
         if (r < L) {
+            const float aq = P.iq[i], ai = P.ik[i];
+            const float sq = srow[0 * 64 + r] + srow[3 * 64 + r];
+            const float sk = srow[1 * 64 + r] + srow[4 * 64 + r];
             const float sc = p.scale;
             const float qdot = sc != 0.f ? sq / (sc * sc) : 0.f;   // (qh . dqh) / scale^2
-            float vq[CPL], vk[CPL];
+            float vq[CPH], vk[CPH];
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
+            for (int e = 0; e < CPH; ++e) {
                 const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
                 vq[e] = aq * (dqh[i][e] - qh * qdot);
                 vk[e] = ai * (dkh[i][e] - kh * sk);
             }
-            const int64_t off = r * rsk + CPL * cl;
-            store_row<TO, CPL>(dqp + off, vq);
-            store_row<TO, CPL>(dkp + off, vk);
-            store_row<TO, CPL>(dgp + off, dG[i]);
-            if (cl == 0) {
+            const int64_t off = r * rsk + ck0;
+            store_row<TO, CPH>(dqp + off, vq);
+            store_row<TO, CPH>(dkp + off, vk);
+            store_row<TO, CPH>(dgp + off, dG[i]);
+            if (wh == 0 && cl == 0) {
+                const float db = srow[2 * 64 + r] + srow[5 * 64 + r];
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
                 dbp[(int64_t)r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
             }
@@ -2126,9 +2168,9 @@ static hipError_t launch_chunk(const BwdParams& p, hipStream_t s) {
             hipLaunchKernelGGL((kda_bwd_chunk_f32_kernel<T, TO, DK, 64>), grid, block, 0, s, p);
     } else {
         if (p.dv == 128)
-            hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 128>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((kda_bwd_grads_kernel<TO, DK, 128>), grid, dim3(kWideThreads), 0, s, p);
         else
-            hipLaunchKernelGGL((kda_bwd_chunk_kernel<T, TO, DK, 64>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((kda_bwd_grads_kernel<TO, DK, 64>), grid, dim3(kWideThreads), 0, s, p);
     }
     return hipGetLastError();
 }
