@@ -19,6 +19,10 @@ HIPCC_FLAGS = [
     "-shared",
     # Packed fp32 VALU instructions are kept out of the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a*b+c is fused only inside one source expression, so every inlined copy
+    # of a step (prologue and loop bodies) rounds the same way and results do
+    # not depend on where a sequence is split.
+    "-ffp-contract=on",
     "-Wno-unused-result",
 ]
 

@@ -450,33 +450,38 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 // bf16 inputs: 8 waves in two groups of four.
 //
 // The state-coupled work of chunk n (U, O, the state update) runs on the four
-// "state" waves, which own the value columns as in the kernel above.  While
-// they run it, the four "prep" waves do all the per-element work of chunk n+1
-// in registers (norms, sigmoid, gate cumulative sum, exp2, the hi/lo operand
-// values) and issue the loads of chunk n+2.  The intra-chunk products, the
-// diagonal inverses and the blocked solve are shared by the two groups.  Each
-// SIMD carries one wave of each group, so the prep waves' VALU work fills the
-// state waves' MFMA and LDS latency.
+// "state" waves, which own the value columns as in the kernel above.  The
+// per-element preparation of chunk n+1 (norms, sigmoid, gate cumsum, exp2, the
+// hi/lo operand values) is split by key columns: the four "prep" waves take the
+// first half and the state waves the second, so the state waves' VALU work
+// fills their MFMA and LDS latency; each group also issues the loads of chunk
+// n+2 for its half.  The two halves' partial row norms meet in LDS.  The
+// intra-chunk products, the diagonal inverses and the blocked solve are shared.
 // ============================================================================
 template <typename TO, int DK, bool SAVE>
 __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
     typedef bf16 T;
     __shared__ FwdSmem<T, DK> sm;
+    __shared__ float snrm[2][2][kChunk];   // [half][q, k][row]: partial sums of squares
     typedef FwdSmem<T, DK> SM;
     constexpr int PK = SM::PK;
     constexpr int PC = SM::PC;
-    constexpr int CPL = DK / 16;    // key columns per lane (prep layout)
-    constexpr int CQ = CPL / 4;     // 4-element groups per lane row
+    constexpr int CPH = DK / 32;    // key columns per lane: half a row per group (prep layout)
     constexpr int VPL = kSlice / 16;
     constexpr int NKB = DK / 32;    // k32 steps over dk
     constexpr int NMB = DK / 16;    // 16-row blocks of the state
-    constexpr int NWB = DK / 64;    // W column blocks per prep wave in the solve
     typedef bf16x8 V8T;
     typedef bf16x4 V4T;
+    typedef __bf16 VH __attribute__((ext_vector_type(CPH)));   // one lane's half-row of bf16 values
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const int tid = threadIdx.x, w = tid >> 6;
+    // Lane coordinates.  refresh() hides the lane index from the optimiser at
+    // the top of every step, so the addresses and masks derived from it are
+    // recomputed per step instead of being held in registers across the loop.
+    int l = tid & 63, qg = l >> 4, cl = l & 15;
     const bool is_state = w < 4;      // wave-uniform
     const int ww = w & 3;             // index inside the group
+    const int hf = is_state ? 1 : 0;  // key-column half this wave prepares
     int chain, slice;
     map_block(blockIdx.x, p.N * p.H, p.nslices, chain, slice);
     const int n = chain / p.H, h = chain % p.H;
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
     const int dv = p.dv, H = p.H;
     const int dv0 = slice * kSlice;
-    const int vcol = dv0 + 16 * ww + cl;   // value column of a state-wave lane
+    int vcol = dv0 + 16 * ww + cl;   // value column of a state-wave lane
 
     const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
     const T* __restrict__ kp = reinterpret_cast<const T*>(p.k);
@@ -494,97 +499,100 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     TO* __restrict__ op = reinterpret_cast<TO*>(p.o);
     const int64_t rs_k = (int64_t)H * DK, rs_v = (int64_t)H * dv;   // token strides
 
-    // ---------------- prep waves: rows 16ww+4qg+i, key columns CPL*cl+e
-    RawRow<T, CPL> rq[4], rk[4], rg[4];   // raw rows of the chunk being prepared
-    RawRow<T, VPL> rv[4];
+    // ---------------- prep layout: rows 16ww+4qg+i, key columns ck0..ck0+CPH-1
+    int r0 = 16 * ww + 4 * qg;
+    int ck0 = hf * (DK / 2) + CPH * cl;
+    int pc0 = perm32(ck0);                  // their (contiguous) tile position
+    auto refresh = [&]() {
+        asm volatile("" : "+v"(l));
+        qg = l >> 4;
+        cl = l & 15;
+        vcol = dv0 + 16 * ww + cl;
+        r0 = 16 * ww + 4 * qg;
+        ck0 = hf * (DK / 2) + CPH * cl;
+        pc0 = perm32(ck0);
+    };
+    RawRow<T, CPH> rq[4], rk[4], rg[4];     // raw rows of the chunk being prepared
+    RawRow<T, VPL> rv[4];                   // (prep waves) its v slice
     RawScalar<T> rb[4];
     float nq[4], nk[4], beta[4];
-    int Lp = 0;                           // valid rows of the chunk being prepared
-    // prepared operand values of the next chunk to run (bf16 hi/lo, 4 columns per vector)
-    V4T xkil[4][CQ];                      // kh/Gam lo of the next chunk
-    float xgc[CPL];                       // Gam_C of the next chunk
+    int Lp = 0;                             // valid rows of the chunk being prepared
+    VH xkil[4];                             // kh/Gam lo of the next chunk to run
+    float xgc[CPH];                         // Gam_C of the next chunk to run
 
     auto load_chunk = [&](int64_t c0) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-        const int r0 = 16 * ww + 4 * qg;
         // uniform chunk bases (scalar registers) + 32-bit per-lane offsets
         const T* qc = qp + c0 * rs_k + h * DK;
         const T* kc = kp + c0 * rs_k + h * DK;
         const T* gc = gp + c0 * rs_k + h * DK;
         const T* vc = vp + c0 * rs_v + h * dv + dv0;
         const T* bc = bp + c0 * H + h;
-        const int ok = r0 * (int)rs_k + CPL * cl, ov = r0 * (int)rs_v + VPL * cl, ob = r0 * H;
+        const int ok = r0 * (int)rs_k + ck0, ov = r0 * (int)rs_v + VPL * cl, ob = r0 * H;
         const int sk = (int)rs_k, sv = (int)rs_v;
-        if (r0 + 4 <= L) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            if (r0 + i < L) {
                 rq[i].load(qc + (ok + i * sk));
                 rk[i].load(kc + (ok + i * sk));
                 rg[i].load(gc + (ok + i * sk));
-                rv[i].load(vc + (ov + i * sv));
+                if (!is_state) rv[i].load(vc + (ov + i * sv));
                 rb[i].load(bc + (ob + i * H));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (r0 + i < L) {
-                    rq[i].load(qc + (ok + i * sk));
-                    rk[i].load(kc + (ok + i * sk));
-                    rg[i].load(gc + (ok + i * sk));
-                    rv[i].load(vc + (ov + i * sv));
-                    rb[i].load(bc + (ob + i * H));
-                } else {
-                    rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
-                    rb[i].zero();
-                }
+            } else {
+                rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
+                rb[i].zero();
             }
         }
         Lp = L;
     };
     // In-wave inclusive prefix of the gates over the wave's 16 rows, for key
-    // column CPL*cl+e: one k16 MFMA of the lower-triangular ones matrix with the
-    // raw bf16 gates, which already sit in B-fragment layout (lane (qg, cl)
-    // holds rows 4qg..4qg+3 of the column).  Exact products, fp32 sums; the
-    // result comes back in the same rows.
-    V4T ltri;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
+    // column ck0+e: one k16 MFMA of the lower-triangular ones matrix with the raw
+    // bf16 gates, which already sit in B-fragment layout (lane (qg, cl) holds
+    // rows 4qg..4qg+3 of the column).  Exact products, fp32 sums; the result
+    // comes back in the same rows.
     auto gate_prefix = [&](int e) {
+        V4T ltri;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
         const V4T b = __builtin_bit_cast(V4T, u16x4{rg[0].x[e], rg[1].x[e], rg[2].x[e], rg[3].x[e]});
         return mma_k16(f32x4{0.f, 0.f, 0.f, 0.f}, ltri, b);
     };
-    // first half of the prep: norms, sigmoid, the wave's gate column sums
+    // first half of the prep: this half's sums of squares, sigmoid, the wave's
+    // gate column sums
     auto prep_a = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
+            for (int e = 0; e < CPH; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
             sq = row16_sum(sq);
             sk = row16_sum(sk);
-            // reciprocal norms (v_rsq, ~1 ulp); the norms themselves are saved
-            nq[i] = __builtin_amdgcn_rsqf(sq + p.eps);
-            nk[i] = __builtin_amdgcn_rsqf(sk + p.eps);
-            const int r = 16 * ww + 4 * qg + i;
-            beta[i] = (r < Lp) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i].f())) : 0.f;
+            if (cl == 0) { snrm[hf][0][r0 + i] = sq; snrm[hf][1][r0 + i] = sk; }
+            beta[i] = (r0 + i < Lp) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i].f())) : 0.f;
         }
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const f32x4 gp = gate_prefix(e);
-            if (qg == 3) sm.red[ww][CPL * cl + e] = gp[3];   // row 15: the wave's column sum
+        for (int e = 0; e < CPH; ++e) {
+            const f32x4 g4 = gate_prefix(e);
+            if (qg == 3) sm.red[ww][ck0 + e] = g4[3];   // row 15: the wave's column sum
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { rq[i].fence(); rk[i].fence(); rg[i].fence(); }
     };
-    // second half (after the prep waves' column sums are in LDS): finish G and
-    // form the operand values.  kh/Gam lo and Gam_C stay in registers until the
-    // chunk's first step (the state waves still read those tiles while this
-    // runs); every other tile is written now.
+    // second half (after both groups' partial sums are in LDS): norms, G and the
+    // operand values.  kh/Gam lo and Gam_C stay in registers until the chunk's
+    // first step (the state waves still read those tiles while this runs); every
+    // other tile is written now.
     auto prep_b = [&](int64_t c0) {
-        float goff[CPL];   // other prep waves' rows above this wave (raw gate units)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int c = CPL * cl + e;
+        for (int i = 0; i < 4; ++i) {
+            // reciprocal norms (v_rsq, ~1 ulp); halves summed in a fixed order
+            nq[i] = __builtin_amdgcn_rsqf(snrm[0][0][r0 + i] + snrm[1][0][r0 + i] + p.eps);
+            nk[i] = __builtin_amdgcn_rsqf(snrm[0][1][r0 + i] + snrm[1][1][r0 + i] + p.eps);
+        }
+        f32x4 G[CPH];   // G[e][i]: gate cumsum (log2 units) at row r0+i, column ck0+e
+#pragma unroll
+        for (int e = 0; e < CPH; ++e) {
+            const int c = ck0 + e;
             float a = 0.f, tot = 0.f;
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {
@@ -592,53 +600,80 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 if (w2 < ww) a += x;
                 tot += x;
             }
-            goff[e] = a;
             xgc[e] = fast_exp2(tot * kLog2e);
-        }
+            const f32x4 g4 = gate_prefix(e);
 #pragma unroll
-        for (int e4 = 0; e4 < CQ; ++e4) {
-            f32x4 G[4];   // G[j][i]: gate cumsum (log2 units) at row 16ww+4qg+i, column CPL*cl+4e4+j
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 gp = gate_prefix(4 * e4 + j);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) G[j][i] = (gp[i] + goff[4 * e4 + j]) * kLog2e;
-            }
-            const int pc = perm32(CPL * cl + 4 * e4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * ww + 4 * qg + i;
-                const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
-                f32x4 vq, vk, vi;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = 4 * e4 + j;
-                    const float gam = fast_exp2(G[j][i]);
-                    const float gin = fast_exp2(-G[j][i]);
-                    vq[j] = (rq[i][e] * aq) * gam;
-                    vk[j] = (rk[i][e] * ak) * gam;
-                    vi[j] = (rk[i][e] * ai) * gin;
-                }
-                sts4_split<T, true>(&sm.qg[r * PK + pc], &sm.qgl[r * PK + pc], vq);
-                const V4T kih = pack4<T>(vi);
-                xkil[i][e4] = pack4<T>(vi - unpack4(kih));
-                *reinterpret_cast<V4T*>(&sm.kg[r * PK + pc]) = pack4<T>(vk);
-                *reinterpret_cast<V4T*>(&sm.ki[r * PK + pc]) = kih;
-            }
+            for (int i = 0; i < 4; ++i) G[e][i] = (g4[i] + a) * kLog2e;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ww + 4 * qg + i;
-            if (cl == 0) sm.beta[r] = beta[i];
-            if (SAVE && slice == 0 && cl == 0 && r < Lp) {
-                p.nq_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nq[i]);
-                p.nk_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nk[i]);
+            const int r = r0 + i;
+            const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
+            float vq[CPH], vk[CPH], vi[CPH];
+#pragma unroll
+            for (int e = 0; e < CPH; ++e) {
+                const float gam = fast_exp2(G[e][i]);
+                const float gin = fast_exp2(-G[e][i]);
+                vq[e] = (rq[i][e] * aq) * gam;
+                vk[e] = (rk[i][e] * ak) * gam;
+                vi[e] = (rk[i][e] * ai) * gin;
+            }
+            VH qh, ql, kg, kih;
+#pragma unroll
+            for (int e = 0; e < CPH; ++e) {
+                qh[e] = from_f32<T>(vq[e]);
+                ql[e] = from_f32<T>(vq[e] - to_f32(qh[e]));
+                kg[e] = from_f32<T>(vk[e]);
+                kih[e] = from_f32<T>(vi[e]);
+                xkil[i][e] = from_f32<T>(vi[e] - to_f32(kih[e]));
+            }
+            *reinterpret_cast<VH*>(&sm.qg[r * PK + pc0]) = qh;
+            *reinterpret_cast<VH*>(&sm.qgl[r * PK + pc0]) = ql;
+            *reinterpret_cast<VH*>(&sm.kg[r * PK + pc0]) = kg;
+            *reinterpret_cast<VH*>(&sm.ki[r * PK + pc0]) = kih;
+        }
+        if (!is_state) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + i;
+                if (cl == 0) sm.beta[r] = beta[i];
+                if (SAVE && slice == 0 && cl == 0 && r < Lp) {
+                    p.nq_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nq[i]);
+                    p.nk_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nk[i]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) {
+                f32x4 x = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
+                sts4<T>(&sm.vt[(VPL * cl + e) * PC + r0], x);   // exact: v is an input value
             }
         }
+    };
+    // step 1 (both groups): the tiles held in registers
+    auto store_held = [&]() {
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-            f32x4 x = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
-            sts4<T>(&sm.vt[(VPL * cl + e) * PC + 16 * ww + 4 * qg], x);   // exact: v is an input value
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<VH*>(&sm.kil[(r0 + i) * PK + pc0]) = xkil[i];
+        if (ww == 0 && qg == 0) {
+#pragma unroll
+            for (int e = 0; e < CPH; ++e) sm.gc[ck0 + e] = xgc[e];
+        }
+    };
+    // step 3 (both groups): Ktil^T = (kh Gam_C / Gam)^T from the kh/Gam hi+lo values
+    // of this half; its lo tile goes where kh/Gam lo lived (read only by step 2)
+    auto store_ktil = [&]() {
+        const int pr = perm32(r0);
+        f32x4 kv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const VH hv = *reinterpret_cast<const VH*>(&sm.ki[(r0 + i) * PK + pc0]);
+#pragma unroll
+            for (int e = 0; e < CPH; ++e) kv[i][e] = to_f32(hv[e]) + to_f32(xkil[i][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < CPH; ++e) {
+            const int c = ck0 + e;
+            f32x4 x = {kv[0][e] * xgc[e], kv[1][e] * xgc[e], kv[2][e] * xgc[e], kv[3][e] * xgc[e]};
+            sts4_split<T, true>(&sm.kt[kt_off(c, pr)], &sm.kil[kt_off(c, pr)], x);
         }
     };
 
@@ -685,9 +720,35 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         for (int i = 0; i < 4; ++i) tii[i] = pack4<T>(*reinterpret_cast<const f32x4*>(&sm.tdiag[i][cl][4 * qg]));
     };
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // W = (I + Akk)^{-1} beta kh Gam for key column block cb, stored negated over the kh/Gam hi tile
+    auto solve_w = [&](int cb, const V4T (&tii)[4]) {
+        const int pc = perm32(16 * cb + cl);
+        f32x4 X[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 acc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = to_f32(sm.kg[(16 * i + 4 * qg + j) * PK + pc]);
+#pragma unroll
+            for (int jp = 0; jp < i; ++jp)
+                acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])), pack4<T>(X[jp]));
+            X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.ki[(16 * i + 4 * qg + j) * PK + pc] = from_f32<T>(-X[i][j]);
+    };
 
-    // The two groups run separate loops with the same barrier sequence: one
-    // barrier after the prologue, then six per chunk.
+    // Prologue: both groups prepare the first chunk.  Then the two groups run
+    // separate loops with the same barrier sequence: six barriers per chunk.
+    if (t0 < t1) {
+        load_chunk(t0);
+        prep_a();
+        lds_barrier();
+        prep_b(t0);
+        if (t0 + kChunk < t1) load_chunk(t0 + kChunk);
+    }
     if (is_state) {
         // ---------------------------------------------------------------- state waves
         const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
@@ -697,11 +758,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
-        if (t0 < t1) lds_barrier();   // prologue (prep waves: first chunk's operand values)
         int64_t slot = t0 / kChunk + n;
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk, ++slot) {
             const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-            // 1: save the entering state of this chunk (fp32)
+            const bool more = c0 + kChunk < t1;
+            refresh();
+            // 1: held tiles; save the entering state of this chunk (fp32)
+            store_held();
             if (SAVE) {
                 float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
 #pragma unroll
@@ -711,9 +774,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             }
             lds_barrier();
             // 2
+            refresh();
             intra_products();
             lds_barrier();
-            // 3: (I + Akk_bb)^{-1}, block b = this wave
+            // 3: (I + Akk_bb)^{-1}, block b = this wave; Ktil^T of this half
+            refresh();
             {
                 const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
                 f32x4 nb;
@@ -723,8 +788,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
             }
+            store_ktil();
             lds_barrier();
             // 4: Ut = (I + Akk)^{-1} diag(beta) v for this wave's 16 value columns
+            //    (and, at dk = 128, W for key column block ww + 4)
+            refresh();
             f32x4 Ut[4];
             {
                 V4T tii[4];
@@ -741,9 +809,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                     Ut[i] = mma_k16(zero, tii[i], ah);
                     Ut[i] = mma_k16(Ut[i], tii[i], pack4<T>(acc - unpack4(ah)));
                 }
+                if constexpr (DK == 128) solve_w(ww + 4, tii);
             }
             lds_barrier();
-            // 5a: U = Ut - W S  (the tile holds -W) ;  O = (qh Gam) S
+            // 5a: U = Ut - W S  (the tile holds -W) ;  O = (qh Gam) S ; next chunk's partial sums
+            refresh();
             f32x4 O[4];
             V8T ufh[2], ufl[2];
             {
@@ -772,8 +842,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
+            if (more) prep_a();
             lds_barrier();
-            // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U
+            refresh();
+            // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U ; next chunk's operand values
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ra = (16 * i + cl) * PC + 8 * qg;
@@ -797,6 +869,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                     S[mb] = mma3<true>(S[mb], lds8<T>(sm.kt + rt), lds8<T>(sm.kil + rt), ufh[kk], ufl[kk]);
                 }
             }
+            if (more) {
+                prep_b(c0 + kChunk);
+                if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);
+            }
             lds_barrier();
         }
         if (p.sfinal) {
@@ -807,82 +883,29 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         }
     } else {
         // ---------------------------------------------------------------- prep waves
-        if (t0 < t1) {
-            load_chunk(t0);
-            prep_a();
-            lds_barrier();
-            prep_b(t0);
-            if (t0 + kChunk < t1) load_chunk(t0 + kChunk);
-        }
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk) {
             const bool more = c0 + kChunk < t1;
-            // 1: the remaining operand tiles of this chunk
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * ww + 4 * qg + i;
-#pragma unroll
-                for (int e4 = 0; e4 < CQ; ++e4)
-                    *reinterpret_cast<V4T*>(&sm.kil[r * PK + perm32(CPL * cl + 4 * e4)]) = xkil[i][e4];
-            }
-            if (ww == 0 && qg == 0) {
-#pragma unroll
-                for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
-            }
+            refresh();
+            store_held();
             lds_barrier();
-            // 2
+            refresh();
             intra_products();
             lds_barrier();
-            // 3: Ktil^T = (kh Gam_C / Gam)^T from the kh/Gam hi+lo values; its lo
-            // tile goes where kh/Gam lo lived (read only by step 2)
-            {
-                const int pr = perm32(16 * ww + 4 * qg);
-#pragma unroll
-                for (int e4 = 0; e4 < CQ; ++e4) {
-                    f32x4 kv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        kv[i] = lds4f<T>(&sm.ki[(16 * ww + 4 * qg + i) * PK + perm32(CPL * cl + 4 * e4)]) +
-                                unpack4(xkil[i][e4]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int e = 4 * e4 + j;
-                        f32x4 x = {kv[0][j] * xgc[e], kv[1][j] * xgc[e], kv[2][j] * xgc[e], kv[3][j] * xgc[e]};
-                        sts4_split<T, true>(&sm.kt[kt_off(CPL * cl + e, pr)], &sm.kil[kt_off(CPL * cl + e, pr)], x);
-                    }
-                }
-            }
+            refresh();
+            store_ktil();
             lds_barrier();
-            // 4: W = (I + Akk)^{-1} beta kh Gam for key column blocks ww + 4cb, stored
-            // negated over the kh/Gam hi tile
+            refresh();
+            // 4: W for key column block ww (and, at dk = 64, that is all of W)
             {
                 V4T tii[4];
                 load_tii(tii);
-#pragma unroll
-                for (int cb = 0; cb < NWB; ++cb) {
-                    const int pc = perm32(16 * (ww + 4 * cb) + cl);
-                    f32x4 X[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        f32x4 acc;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[j] = to_f32(sm.kg[(16 * i + 4 * qg + j) * PK + pc]);
-#pragma unroll
-                        for (int jp = 0; jp < i; ++jp)
-                            acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])),
-                                          pack4<T>(X[jp]));
-                        X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sm.ki[(16 * i + 4 * qg + j) * PK + pc] = from_f32<T>(-X[i][j]);
-                }
+                solve_w(ww, tii);
             }
             lds_barrier();
-            // 5a: norms, sigmoid and in-wave gate sums of the next chunk
+            refresh();
             if (more) prep_a();
             lds_barrier();
-            // 5b: operand values of the next chunk; loads of the one after
+            refresh();
             if (more) {
                 prep_b(c0 + kChunk);
                 if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);

@@ -21,6 +21,9 @@ run dtype; the oracle upcasts them exactly to float64.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 BLOCK = 1 << 16
@@ -42,11 +45,17 @@ WORKLOADS = {
 
 
 def round_bf16(x) -> np.ndarray:
-    """Round to bfloat16 (round-to-nearest-even via float32); returns float32."""
+    """Round to bfloat16 (round-to-nearest-even via float32); returns float32.
+
+    Finite inputs only: the 32-bit sum below cannot carry out of a finite
+    float32's bit pattern."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+    u = f.view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r &= 0xFFFF0000
+    return r.view(np.float32).reshape(f.shape)
 
 
 def round_to(x, dtype: str) -> np.ndarray:
@@ -57,13 +66,40 @@ def round_to(x, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def _normal_tokens(seed, tid, T, tail_shape, mean=0.0, std=1.0):
-    """[T, *tail_shape] normals drawn in 65,536-token blocks."""
-    out = np.empty((T,) + tuple(tail_shape), dtype=np.float64)
-    for blk in range((T + BLOCK - 1) // BLOCK):
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _normal_tokens(seed, tid, T, tail_shape, dtype, mean=0.0, std=1.0, transform=None):
+    """[T, *tail_shape] float32: normals drawn in float64 in 65,536-token
+    blocks, each passed through ``transform`` (elementwise, float64) and
+    rounded to ``dtype``.  Blocks have their own generators, so they are drawn
+    in parallel threads; inside a block the stream is consumed in order through
+    one small reused buffer.  The values depend on neither."""
+    tail = tuple(tail_shape)
+    out = np.empty((T,) + tail, dtype=np.float32)
+    step = max(1, (1 << 21) // max(1, int(np.prod(tail, dtype=np.int64))))
+
+    def one(blk):
         a, z = blk * BLOCK, min((blk + 1) * BLOCK, T)
         rng = np.random.default_rng([seed, tid, blk])
-        out[a:z] = rng.normal(mean, std, size=(z - a,) + tuple(tail_shape))
+        buf = np.empty((min(step, z - a),) + tail, dtype=np.float64)
+        for s in range(a, z, step):
+            x = buf[: min(step, z - s)]
+            rng.standard_normal(out=x)   # the same stream as rng.normal(mean, std, size)
+            x *= std
+            x += mean
+            if transform is not None:
+                x = transform(x)
+            out[s : s + x.shape[0]] = round_to(x, dtype)
+
+    nblk = (T + BLOCK - 1) // BLOCK
+    if nblk <= 1:
+        for blk in range(nblk):
+            one(blk)
+    else:
+        with ThreadPoolExecutor(max_workers=min(_workers(), nblk)) as ex:
+            list(ex.map(one, range(nblk)))
     return out
 
 
@@ -103,22 +139,23 @@ def generate(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, num_seqs: 
 
     out = {}
     if need("q"):
-        out["q"] = round_to(_normal_tokens(seed, TENSOR_IDS["q"], T, (H, dk)), dtype)
+        out["q"] = _normal_tokens(seed, TENSOR_IDS["q"], T, (H, dk), dtype)
     if need("k"):
-        out["k"] = round_to(_normal_tokens(seed, TENSOR_IDS["k"], T, (H, dk)), dtype)
+        out["k"] = _normal_tokens(seed, TENSOR_IDS["k"], T, (H, dk), dtype)
     if need("v"):
-        out["v"] = round_to(_normal_tokens(seed, TENSOR_IDS["v"], T, (H, dv)), dtype)
+        out["v"] = _normal_tokens(seed, TENSOR_IDS["v"], T, (H, dv), dtype)
     if need("b"):
-        out["b"] = round_to(_normal_tokens(seed, TENSOR_IDS["b"], T, (H,)), dtype)
+        out["b"] = _normal_tokens(seed, TENSOR_IDS["b"], T, (H,), dtype)
     if need("g"):
-        x = _normal_tokens(seed, TENSOR_IDS["g"], T, (H, dk), mean=-2.0)
-        out["g"] = round_to(-np.logaddexp(0.0, x), dtype)   # -softplus(x)
+        # -softplus(x), x ~ N(-2, 1)
+        out["g"] = _normal_tokens(seed, TENSOR_IDS["g"], T, (H, dk), dtype, mean=-2.0,
+                                  transform=lambda x: -np.logaddexp(0.0, x))
     if with_s0 and need("s0"):
         rng = np.random.default_rng([seed, TENSOR_IDS["s0"], 0])
         out["s0"] = rng.normal(0.0, 0.1, size=(num_seqs, H, dk, dv)).astype(np.float32)
     if with_grads:
         if need("dO"):
-            out["dO"] = round_to(_normal_tokens(seed, TENSOR_IDS["dO"], T, (H, dv)), dtype)
+            out["dO"] = _normal_tokens(seed, TENSOR_IDS["dO"], T, (H, dv), dtype)
         if need("dS"):
             rng = np.random.default_rng([seed, TENSOR_IDS["dS"], 0])
             out["dS"] = rng.normal(0.0, 0.1, size=(num_seqs, H, dk, dv)).astype(np.float32)

@@ -148,12 +148,17 @@ def test_w2_forward_sampled_chains():
         assert e1 <= 2e-2 and e2 <= 1e-2
 
 
+@pytest.mark.timeout(900)
 def test_w3_long_context_sampled_head():
+    # about a minute of input generation and another of the fp64 oracle over
+    # one 1M-token head; each phase reports when it ends
     need_gpu()
     _say("workload 3 forward: bf16 B=1 H=16 T=1048576 d=128 (one sampled head)")
     spec, cu, x = kda_inputs.workload(3)
+    _say("w3 inputs generated")
     o, sf, *_ = run_fwd(x, "bf16", cu=cu)
     o, sf = host(o), host(sf)
+    _say("w3 GPU forward done")
     h = 5
     o_ref, sf_ref = _oracle_heads(x, cu, [h])
     from gpu_util import frob_rel, max_over_rms
