@@ -21,6 +21,11 @@ implementation saves or recomputes is not counted), per kernel:
   chunk gradients per token-head: q, k, g, v, beta, dO (bf16) + dq, dk, dg, dv,
                   dbeta (fp32)
   state scan      per (sequence, head): dS_final in, d(initial state) out
+  decode step     per (sequence, head): the fp32 state read and written once,
+                  q, k, g (dk bf16 each) + v (dv bf16) + beta in, o (dv fp32) out
+
+`decode` reports the serving step on its own: 256 sequences x 32 heads, d = 128,
+bf16 token inputs, the fp32 state updated in place, one token per call.
 """
 import argparse
 import json
@@ -63,11 +68,19 @@ def traffic_record(kernel):
     return rec["bytes_per_launch"]
 
 
+DECODE_N = 256   # sequences in the timed decode batch (H, dk, dv as the workload)
+
+
+def decode_bytes(N, H, dk, dv):
+    return N * H * (2 * dk * dv * 4 + (3 * dk + dv + 1) * 2 + dv * 4)
+
+
 KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file)
     "grads": ("kda_bwd_grads_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
     "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
     "fwd": ("kda_fwd_bf16_kernel<float, 128, true>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
     "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
+    "decode": ("kda_decode_kernel", "gated_delta_rule_41_amd/csrc/kda_decode.hip"),
 }
 
 
@@ -236,6 +249,31 @@ def main():
     torch.cuda.synchronize()
     inf_ms = e0.elapsed_time(e1) / n_inf
 
+    # the decode step on its own: one token per sequence, state updated in place
+    xd = kda_inputs.generate(1005, DECODE_N, H, dk, dv, "bf16", num_seqs=DECODE_N, with_s0=True)
+    dq_, dk_, dv_, dg_, db_ = (to_dev(xd[n]) for n in ("q", "k", "v", "g", "b"))
+    sd = torch.from_numpy(xd["s0"]).to(dev)
+    del xd
+    od = torch.empty((DECODE_N, H, dv), dtype=torch.float32, device=dev)
+    kda.kda_decode(dq_, dk_, dv_, dg_, db_, sd, out_state=sd)   # checks shapes once
+    # the timed loop calls the C ABI directly with prepared arguments, so host
+    # overhead per call stays well under the kernel's duration
+    from gated_delta_rule_41_amd import _lib
+    dcfg = _lib.make_config(H, dk, dv, kda.KDA_BF16, kda.KDA_F32)
+    dargs = (dcfg, DECODE_N) + tuple(int(t.data_ptr()) for t in (dq_, dk_, dv_, dg_, db_, sd, sd, od)) + \
+        (stream.cuda_stream,)
+    for _ in range(3):
+        _lib.check(_lib.kda_decode_raw(*dargs))
+    n_dec = max(20, 2 * args.steps)
+    e0.record(stream)
+    for _ in range(n_dec):
+        _lib.kda_decode_raw(*dargs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / n_dec
+    dec_bytes = decode_bytes(DECODE_N, H, dk, dv)
+    del sd
+
     tokens = B * T
     names = {"fwd": "kda_fwd_bf16_kernel (training forward, state save)",
              "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
@@ -272,6 +310,12 @@ def main():
                          "achieved": f_bytes / (inf_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes},
+        "decode": {"workload": f"decode-bf16-N{DECODE_N}-H{H}-d{dk} (fp32 state in place)",
+                   "us_per_step": dec_ms * 1e3, "tokens_per_s": DECODE_N / (dec_ms * 1e-3),
+                   "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": dec_bytes / (dec_ms * 1e-3) / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "traffic": traffic_record("decode"), "alg_bytes_per_launch": dec_bytes}},
         "timed_wall_s": wall,
     }
     if args.copy_probe_mib > 0:

@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KdaConfig, KdaError, kda_bwd_workspace_size,
                    kda_fwd_workspace_size, kda_saved_size, make_config)
 
-__all__ = ["kda_fwd", "kda_bwd", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
+__all__ = ["kda_fwd", "kda_bwd", "kda_decode", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
            "make_config", "KdaConfig", "KdaError", "KDA_F32", "KDA_BF16", "KDA_FLAG_SAVE_FOR_BWD"]
 
 
@@ -146,3 +146,37 @@ def kda_bwd(q, k, v, g, beta, saved, dO, cu_seqlens=None, initial_state=None, dS
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
                                     _ptr(out["dS0"]), _ptr(ws), wsb, stream, stage))
     return out
+
+
+def kda_decode(q, k, v, g, beta, state=None, *, out_state=None, out_dtype=None, eps: float = 1e-6,
+               scale: float = 1.0):
+    """One decode step: one token per sequence on a resident fp32 state.
+
+    q, k, g ``[N, H, dk]``, v ``[N, H, dv]``, beta ``[N, H]`` (the logit);
+    ``state`` ``[N, H, dk, dv]`` fp32 or None (zero state).  ``out_state`` is
+    where the state after the token goes: a new tensor if None, or a given
+    tensor, which may be ``state`` itself for an in-place update.  Returns
+    ``(o, out_state)``."""
+    torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [N,H,dk] and v [N,H,dv]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("libkda runs on the GPU only: tensors must be on a cuda (HIP) device")
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)), ("g", g, (N, H, dk)),
+                         ("beta", beta, (N, H))):
+        _check(t, name, shp, dt, dev)
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if out_state is None:
+        out_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(out_state, "out_state", (N, H, dk, dv), torch.float32, dev)
+    out_dtype = out_dtype or torch.float32
+    cfg = make_config(H, dk, dv, _dt_code(dt), _dt_code(out_dtype), eps, scale, 0)
+    o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.check(_lib.kda_decode_raw(cfg, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                       _ptr(out_state), _ptr(o), stream))
+    return o, out_state

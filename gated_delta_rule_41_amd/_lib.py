@@ -72,6 +72,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 17 + [ctypes.c_size_t, _vp]
         fn.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [cfgp, ctypes.c_int32] + [_vp] * 9
+    lib.kda_decode.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -126,3 +128,8 @@ def kda_bwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initi
     fn = getattr(load(), BWD_ENTRY[stage])
     return fn(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved,
               dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream)
+
+
+def kda_decode_raw(cfg, num_seqs, q, k, v, g, beta, state_in, state_out, o, stream) -> int:
+    """Direct call of kda_decode with integer device addresses (0 = NULL); returns the status."""
+    return load().kda_decode(ctypes.byref(cfg), num_seqs, q, k, v, g, beta, state_in, state_out, o, stream)

@@ -11,6 +11,12 @@
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
+#define KDA_TRY_(x)                      \
+    do {                                 \
+        kda_status _s = (x);             \
+        if (_s != KDA_OK) return _s;     \
+    } while (0)
+
 namespace {
 
 thread_local char g_err[256] = "";
@@ -29,7 +35,8 @@ size_t state_elem_bytes(const kda_config* c) { (void)c; return 4; }
 
 // Config check shared by every entry point.  Returns KDA_OK or a status with
 // the reason left in g_err.
-kda_status check_config(const kda_config* c) {
+// Everything but the chunk kernels' dtype/dim restriction (the decode step has none).
+kda_status check_config_common(const kda_config* c) {
     if (!c) return fail(KDA_ERR_INVALID_ARG, "config is NULL%s");
     if (c->H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1%s");
     if ((c->dk != 64 && c->dk != 128) || (c->dv != 64 && c->dv != 128))
@@ -38,11 +45,17 @@ kda_status check_config(const kda_config* c) {
     if ((c->in_dtype != KDA_F32 && c->in_dtype != KDA_BF16) ||
         (c->out_dtype != KDA_F32 && c->out_dtype != KDA_BF16))
         return fail(KDA_ERR_INVALID_ARG, "unknown dtype%s");
-    if (c->in_dtype == KDA_F32 && c->dk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "fp32 inputs support dk = 64 only%s");
     if (!(c->l2_eps >= 0.f) || !isfinite(c->l2_eps)) return fail(KDA_ERR_INVALID_ARG, "l2_eps must be finite and >= 0%s");
     if (!isfinite(c->scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite%s");
     if (c->flags & ~KDA_FLAG_SAVE_FOR_BWD) return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
+    return KDA_OK;
+}
+
+// Config check shared by the chunked entry points.
+kda_status check_config(const kda_config* c) {
+    KDA_TRY_(check_config_common(c));
+    if (c->in_dtype == KDA_F32 && c->dk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "fp32 inputs support dk = 64 only%s");
     return KDA_OK;
 }
 
@@ -97,11 +110,7 @@ size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
 
 }  // namespace
 
-#define KDA_TRY(x)                       \
-    do {                                 \
-        kda_status _s = (x);             \
-        if (_s != KDA_OK) return _s;     \
-    } while (0)
+#define KDA_TRY(x) KDA_TRY_(x)
 
 extern "C" {
 
@@ -175,6 +184,42 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     p.eps = cfg->l2_eps; p.scale = cfg->scale;
     p.nslices = cfg->dv / kda::kSlice;
     hipError_t e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+kda_status kda_decode(const kda_config* cfg, int32_t N, const void* q, const void* k, const void* v,
+                      const void* g, const void* beta, const float* state_in, float* state_out, void* o,
+                      void* stream) {
+    g_err[0] = 0;
+    KDA_TRY(check_config_common(cfg));
+    if (N < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0%s");
+    if ((int64_t)N * cfg->H * (cfg->dv / kda::kSlice) >= ((int64_t)1 << 31))
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large%s");
+    if (N > 0) {
+        KDA_TRY(need_ptr(q, "q"));
+        KDA_TRY(need_ptr(k, "k"));
+        KDA_TRY(need_ptr(v, "v"));
+        KDA_TRY(need_ptr(g, "g"));
+        KDA_TRY(need_ptr(beta, "beta"));
+        KDA_TRY(need_ptr(state_out, "state_out"));
+        KDA_TRY(need_ptr(o, "o"));
+    }
+    KDA_TRY(opt_ptr(state_in, "state_in"));
+    if (state_in && state_in != state_out) {
+        const size_t bytes = (size_t)N * cfg->H * cfg->dk * cfg->dv * sizeof(float);
+        const char *a = (const char*)state_in, *b = (const char*)state_out;
+        if (a < b + bytes && b < a + bytes)
+            return fail(KDA_ERR_INVALID_ARG, "state_in and state_out overlap without being equal%s");
+    }
+    kda::DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.b = beta;
+    p.s_in = state_in; p.s_out = state_out; p.o = o;
+    p.N = N; p.H = cfg->H; p.dv = cfg->dv;
+    p.eps = cfg->l2_eps; p.scale = cfg->scale;
+    p.nslices = cfg->dv / kda::kSlice;
+    hipError_t e = kda::launch_decode(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }

@@ -71,11 +71,26 @@ struct BwdParams {
     int32_t nslices;
 };
 
+struct DecodeParams {
+    const void* q;       // [N,H,dk] one token per sequence
+    const void* k;
+    const void* v;       // [N,H,dv]
+    const void* g;
+    const void* b;       // [N,H]
+    const float* s_in;   // [N,H,dk,dv] or nullptr (zero state)
+    float* s_out;        // [N,H,dk,dv]; may equal s_in
+    void* o;             // [N,H,dv] out dtype
+    int32_t N, H, dv;
+    float eps, scale;
+    int32_t nslices;     // dv / kSlice
+};
+
 // in_dtype / out_dtype: 0 = fp32, 1 = bf16 (kda_dtype values).
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save,
                       hipStream_t stream);
 // Backward stages (bit mask): the reverse state scan, then the chunk-parallel gradients.
 constexpr int kBwdScan = 1, kBwdGrads = 2;
 hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, int stages, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int in_dtype, int out_dtype, int dk, hipStream_t stream);
 
 }  // namespace kda

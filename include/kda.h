@@ -154,6 +154,27 @@ kda_status kda_bwd_grads(const kda_config* cfg, int64_t total_tokens, int32_t nu
                          void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Decode step: one token per sequence on a resident state (serving).  For
+ * every sequence n and head h it applies one step of the recurrence above to
+ * the state entering the token and returns that token's output, reading and
+ * writing the state once (the pages report KDA inside the serving frameworks
+ * with prefill and decode run apart: "Moore Threads добавила поддержку Kimi
+ * K3.1 Pro на GPU MTT S5000", lt.allworld.media 191952736, section
+ * "Поддержка в фреймворках и новые возможности").  A run of calls over the
+ * tokens of a sequence equals kda_fwd on that sequence up to rounding.
+ *   q, k, g : [num_seqs, H, dk]   v : [num_seqs, H, dv]   beta : [num_seqs, H]
+ *             (in_dtype; one token per sequence; beta is the logit)
+ *   state_in  : fp32 [num_seqs, H, dk, dv], or NULL for the zero state
+ *   state_out : fp32 [num_seqs, H, dk, dv], the state after the token; it may
+ *               be state_in itself (in-place update) but must not otherwise
+ *               overlap it (KDA_ERR_INVALID_ARG)
+ *   o         : [num_seqs, H, dv] in out_dtype
+ * cfg->chunk and cfg->flags are checked as for kda_fwd but not used; fp32
+ * inputs are supported for dk = 64 and 128.  num_seqs = 0 enqueues nothing. */
+kda_status kda_decode(const kda_config* cfg, int32_t num_seqs, const void* q, const void* k, const void* v,
+                      const void* g, const void* beta, const float* state_in, float* state_out, void* o,
+                      void* stream);
+
 /* Static description of a status code. */
 const char* kda_status_string(kda_status s);
 /* Thread-local description of the last failure on this thread ("" if none). */

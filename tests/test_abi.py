@@ -128,3 +128,28 @@ def test_python_layer_refuses_cpu_tensors():
         kda.kda_fwd(x, x, x, x, torch.zeros(4, 1))
     assert KDA_OK == 0
     assert isinstance(_lib.KdaConfig(), ctypes.Structure)
+
+
+def _decode(cfg, N=2, q=FAKE, s_in=0, s_out=FAKE, o=FAKE):
+    return _lib.kda_decode_raw(cfg, N, q, FAKE, FAKE, FAKE, FAKE, s_in, s_out, o, 0)
+
+
+def test_decode_rejects_bad_arguments():
+    lib = _lib.load()
+    assert lib.kda_decode(None, 1, *([None] * 9)) == KDA_ERR_INVALID_ARG
+    cfg = _lib.make_config(4, 128, 128, KDA_BF16)
+    assert _decode(cfg, N=-1) == KDA_ERR_INVALID_ARG
+    assert _decode(cfg, q=0) == KDA_ERR_INVALID_ARG and "q" in _err()
+    assert _decode(cfg, o=0) == KDA_ERR_INVALID_ARG and "o" in _err()
+    assert _decode(cfg, s_out=0) == KDA_ERR_INVALID_ARG and "state_out" in _err()
+    assert _decode(cfg, s_out=FAKE + 4) == KDA_ERR_INVALID_ARG and "aligned" in _err()
+    assert _decode(cfg, s_in=FAKE + 8) == KDA_ERR_INVALID_ARG and "state_in" in _err()
+    # overlapping but distinct state buffers are refused; the same buffer (in place) is not
+    assert _decode(cfg, s_in=FAKE, s_out=FAKE + 4096) == KDA_ERR_INVALID_ARG and "overlap" in _err()
+    cfg.dk = 96
+    assert _decode(cfg) == KDA_ERR_UNSUPPORTED
+    cfg.dk, cfg.in_dtype = 128, 9
+    assert _decode(cfg) == KDA_ERR_INVALID_ARG
+    # nothing to do: returns before any HIP call
+    cfg.in_dtype = KDA_F32
+    assert _decode(cfg, N=0, q=0, s_out=0, o=0) == KDA_OK
