@@ -16,11 +16,12 @@ from __future__ import annotations
 from typing import Optional
 
 from . import _lib
-from ._lib import (KDA_BF16, KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KdaConfig, KdaError, kda_bwd_workspace_size,
+from ._lib import (KDA_BF16, KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KDA_FLAG_SEQUENTIAL, KdaConfig, KdaError, kda_bwd_workspace_size,
                    kda_fwd_workspace_size, kda_saved_size, make_config)
 
 __all__ = ["kda_fwd", "kda_bwd", "kda_decode", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
-           "make_config", "KdaConfig", "KdaError", "KDA_F32", "KDA_BF16", "KDA_FLAG_SAVE_FOR_BWD"]
+           "make_config", "KdaConfig", "KdaError", "KDA_F32", "KDA_BF16", "KDA_FLAG_SAVE_FOR_BWD",
+           "KDA_FLAG_SEQUENTIAL"]
 
 
 def _torch():
@@ -78,16 +79,17 @@ def _common(q, k, v, g, beta, cu_seqlens, num_seqs):
 
 def kda_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: Optional[int] = None,
             out_dtype=None, save_for_bwd: bool = False, eps: float = 1e-6, scale: float = 1.0,
-            output_final_state: bool = True):
+            output_final_state: bool = True, sequential: bool = False):
     """KDA forward.  Returns ``(o, final_state, saved)``; ``saved`` is None
     unless ``save_for_bwd``.  ``num_seqs`` splits an un-packed stream into equal
-    sequences when ``cu_seqlens`` is None."""
+    sequences when ``cu_seqlens`` is None.  ``sequential`` keeps the library
+    from splitting long sequences into segments (KDA_FLAG_SEQUENTIAL)."""
     torch = _torch()
     T, H, dk, dv, N, dev, dt = _common(q, k, v, g, beta, cu_seqlens, num_seqs)
     out_dtype = out_dtype or torch.float32
     _check(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
     cfg = make_config(H, dk, dv, _dt_code(dt), _dt_code(out_dtype), eps, scale,
-                      KDA_FLAG_SAVE_FOR_BWD if save_for_bwd else 0)
+                      (KDA_FLAG_SAVE_FOR_BWD if save_for_bwd else 0) | (KDA_FLAG_SEQUENTIAL if sequential else 0))
     o = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
     sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     saved = None

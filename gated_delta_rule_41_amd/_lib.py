@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SAVE_FOR_BWD = 1
+KDA_FLAG_SEQUENTIAL = 2
 
 
 class KdaConfig(ctypes.Structure):

@@ -47,7 +47,7 @@ kda_status check_config_common(const kda_config* c) {
         return fail(KDA_ERR_INVALID_ARG, "unknown dtype%s");
     if (!(c->l2_eps >= 0.f) || !isfinite(c->l2_eps)) return fail(KDA_ERR_INVALID_ARG, "l2_eps must be finite and >= 0%s");
     if (!isfinite(c->scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite%s");
-    if (c->flags & ~KDA_FLAG_SAVE_FOR_BWD) return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
+    if (c->flags & ~(KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL)) return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
     return KDA_OK;
 }
 
@@ -103,6 +103,48 @@ SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
     return s;
 }
 
+// ---------------------------------------------------------------- two-level forward
+// Few long sequences leave most compute units idle in the one-pass forward
+// (one workgroup per sequence, head and value slice).  Then every document is
+// split into segments (see kda_split.hip).  The plan depends on the config and
+// the sizes only, so the workspace size is a pure host function.
+constexpr int64_t kSplitMaxChains = 128;   // split only below this many (sequence, head, slice) chains
+constexpr int64_t kSplitTargetWGs = 1024;  // aim for this many workgroups in the per-segment passes
+constexpr int64_t kMinSegment = 4096;      // tokens; shorter segments spend more on maps than they save
+
+struct SplitPlan {
+    bool on;
+    int32_t seg_len, P;   // segment length (multiple of the chunk) and segment capacity
+    size_t seg_cu, doc_seg, sf_dst, maps, s_in, total;   // workspace offsets
+};
+
+SplitPlan split_plan(const kda_config* c, int64_t T, int32_t N) {
+    SplitPlan s;
+    memset(&s, 0, sizeof s);
+    if (c->in_dtype != KDA_BF16 || (c->flags & (KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL)) || N < 1 || T < 1)
+        return s;
+    const int64_t chains = (int64_t)N * c->H * (c->dv / kda::kSlice);
+    if (chains >= kSplitMaxChains) return s;
+    const int64_t avg = T / N;
+    const int64_t per_doc = (kSplitTargetWGs + chains - 1) / chains;
+    int64_t L = (avg + per_doc - 1) / per_doc;
+    L = (L + kda::kChunk - 1) / kda::kChunk * kda::kChunk;
+    if (L < kMinSegment) L = kMinSegment;
+    if (avg < 2 * L) return s;
+    const int64_t P = T / L + N;
+    if (P * c->H * ((c->dk + c->dv) / kda::kSlice) >= ((int64_t)1 << 31)) return s;
+    s.on = true;
+    s.seg_len = (int32_t)L;
+    s.P = (int32_t)P;
+    s.seg_cu = 0;
+    s.doc_seg = align256((size_t)(P + 1) * 4);
+    s.sf_dst = s.doc_seg + align256((size_t)(N + 1) * 4);
+    s.maps = s.sf_dst + align256((size_t)P * 4);
+    s.s_in = s.maps + align256((size_t)P * c->H * c->dk * (c->dk + c->dv) * sizeof(float));
+    s.total = s.s_in + align256((size_t)P * c->H * c->dk * c->dv * sizeof(float));
+    return s;
+}
+
 // dL/dS at the end of every chunk (state type), then dU of every chunk.
 size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
     return align256((size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c));
@@ -134,8 +176,8 @@ size_t kda_saved_size(const kda_config* cfg, int64_t T, int32_t N) {
 }
 
 size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
-    (void)cfg; (void)T; (void)N;
-    return 0;
+    if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
+    return split_plan(cfg, T, N).total;
 }
 
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
@@ -164,8 +206,9 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     KDA_TRY(opt_ptr(workspace, "workspace"));
     const bool save = (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) != 0;
     if (save) KDA_TRY(need_ptr(saved, "saved"));
-    if (workspace_bytes < kda_fwd_workspace_size(cfg, T, N))
-        return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
+    const size_t ws_need = kda_fwd_workspace_size(cfg, T, N);
+    if (workspace_bytes < ws_need) return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
+    if (ws_need > 0) KDA_TRY(need_ptr(workspace, "workspace"));
 
     kda::FwdParams p;
     memset(&p, 0, sizeof p);
@@ -183,7 +226,39 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     p.seqlen = cu ? 0 : (int32_t)(T / N);
     p.eps = cfg->l2_eps; p.scale = cfg->scale;
     p.nslices = cfg->dv / kda::kSlice;
-    hipError_t e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, (hipStream_t)stream);
+    const SplitPlan sp = split_plan(cfg, T, N);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (!sp.on) {
+        e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, st);
+    } else {
+        char* ws = (char*)workspace;
+        int32_t* seg_cu = (int32_t*)(ws + sp.seg_cu);
+        int32_t* doc_seg = (int32_t*)(ws + sp.doc_seg);
+        int32_t* sf_dst = (int32_t*)(ws + sp.sf_dst);
+        float* maps = (float*)(ws + sp.maps);
+        float* s_in = (float*)(ws + sp.s_in);
+        kda::SegParams sg = {cu, seg_cu, doc_seg, sf_dst, T, N, p.seqlen, sp.seg_len, sp.P};
+        e = kda::launch_segments(sg, st);
+        if (e == hipSuccess) {   // every segment's [M | B] from the zero state
+            kda::FwdParams pm = p;
+            pm.cu = seg_cu; pm.N = sp.P; pm.seqlen = 0;
+            pm.s0 = nullptr; pm.o = nullptr; pm.sfinal = maps; pm.sf_dst = nullptr;
+            pm.nslices = (cfg->dk + cfg->dv) / kda::kSlice;
+            pm.map_slices = cfg->dk / kda::kSlice;
+            e = kda::launch_fwd_maps(pm, cfg->dk, st);
+        }
+        if (e == hipSuccess) {   // the state entering every segment
+            kda::CarryParams cp = {doc_seg, s0, maps, s_in, N, cfg->H, cfg->dv, cfg->dv / kda::kSlice};
+            e = kda::launch_carry(cp, cfg->dk, st);
+        }
+        if (e == hipSuccess) {   // the segments from their entering states
+            kda::FwdParams pc = p;
+            pc.cu = seg_cu; pc.N = sp.P; pc.seqlen = 0;
+            pc.s0 = s_in; pc.sf_dst = sf_dst;
+            e = kda::launch_fwd(pc, cfg->in_dtype, cfg->out_dtype, cfg->dk, false, st);
+        }
+    }
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }

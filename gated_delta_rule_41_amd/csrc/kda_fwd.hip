@@ -457,8 +457,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
 // fills their MFMA and LDS latency; each group also issues the loads of chunk
 // n+2 for its half.  The two halves' partial row norms meet in LDS.  The
 // intra-chunk products, the diagonal inverses and the blocked solve are shared.
+//
+// MAP = true is the first level of the two-level forward for long sequences:
+// each "sequence" is a segment, and the workgroup computes a slice of the
+// segment's affine map S_out = M S_in + B.  The state is [M | B] (dk x
+// (dk + dv)): slices [0, dk/64) start from the identity with zero values and
+// give M, the others start from zero with the real values and give B.  Nothing
+// but that state is written.
 // ============================================================================
-template <typename TO, int DK, bool SAVE>
+template <typename TO, int DK, bool SAVE, bool MAP>
 __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams p) {
     typedef bf16 T;
     __shared__ FwdSmem<T, DK> sm;
@@ -488,8 +495,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     int64_t t0, t1;
     seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
     const int dv = p.dv, H = p.H;
-    const int dv0 = slice * kSlice;
+    const bool mslice = MAP && slice < p.map_slices;           // this slice carries M
+    const int dv0 = MAP ? (mslice ? 0 : (slice - p.map_slices) * kSlice) : slice * kSlice;
+    const int ld = MAP ? DK + dv : dv;                         // row stride of the state arrays
+    const int sc0 = MAP ? slice * kSlice : dv0;                // first state column of the slice
     int vcol = dv0 + 16 * ww + cl;   // value column of a state-wave lane
+    int scol = sc0 + 16 * ww + cl;   // its state column
 
     const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
     const T* __restrict__ kp = reinterpret_cast<const T*>(p.k);
@@ -508,6 +519,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         qg = l >> 4;
         cl = l & 15;
         vcol = dv0 + 16 * ww + cl;
+        scol = sc0 + 16 * ww + cl;
         r0 = 16 * ww + 4 * qg;
         ck0 = hf * (DK / 2) + CPH * cl;
         pc0 = perm32(ck0);
@@ -536,7 +548,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 rq[i].load(qc + (ok + i * sk));
                 rk[i].load(kc + (ok + i * sk));
                 rg[i].load(gc + (ok + i * sk));
-                if (!is_state) rv[i].load(vc + (ov + i * sv));
+                if (!is_state) {
+                    if (mslice) rv[i].zero();
+                    else rv[i].load(vc + (ov + i * sv));
+                }
                 rb[i].load(bc + (ob + i * H));
             } else {
                 rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
@@ -751,13 +766,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     }
     if (is_state) {
         // ---------------------------------------------------------------- state waves
-        const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
+        const int64_t sbase = ((int64_t)n * H + h) * DK * ld;
         f32x4 S[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mb + 4 * qg + i;
+                if (MAP)
+                    S[mb][i] = (mslice && row == scol) ? 1.f : 0.f;
+                else
+                    S[mb][i] = p.s0 ? p.s0[sbase + (int64_t)row * dv + vcol] : 0.f;
+            }
         int64_t slot = t0 / kChunk + n;
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk, ++slot) {
             const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
@@ -856,7 +876,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * i + 4 * qg + j;
-                    if (r < L) op[((c0 + r) * H + h) * dv + vcol] = from_f32<TO>(O[i][j]);
+                    if (!MAP && r < L) op[((c0 + r) * H + h) * dv + vcol] = from_f32<TO>(O[i][j]);
                 }
             }
 #pragma unroll
@@ -875,11 +895,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             }
             lds_barrier();
         }
-        if (p.sfinal) {
+        const int nd = p.sf_dst ? p.sf_dst[n] : n;   // the row of sfinal this sequence ends
+        if (p.sfinal && nd >= 0) {
+            const int64_t fbase = ((int64_t)nd * H + h) * DK * ld;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p.sfinal[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+                for (int i = 0; i < 4; ++i) p.sfinal[fbase + (int64_t)(16 * mb + 4 * qg + i) * ld + scol] = S[mb][i];
         }
     } else {
         // ---------------------------------------------------------------- prep waves
@@ -920,15 +942,24 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool save, hipStream_t s) {
     const dim3 grid((unsigned)(p.N * p.H * p.nslices));
     if constexpr (std::is_same<T, bf16>::value) {
         if (save)
-            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, true>), grid, dim3(kWideThreads), 0, s, p);
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, true, false>), grid, dim3(kWideThreads), 0, s, p);
         else
-            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, false>), grid, dim3(kWideThreads), 0, s, p);
+            hipLaunchKernelGGL((kda_fwd_bf16_kernel<TO, DK, false, false>), grid, dim3(kWideThreads), 0, s, p);
     } else {
         if (save)
             hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, true>), grid, dim3(kThreads), 0, s, p);
         else
             hipLaunchKernelGGL((kda_fwd_kernel<T, TO, DK, false>), grid, dim3(kThreads), 0, s, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t s) {
+    const dim3 grid((unsigned)(p.N * p.H * p.nslices));
+    if (dk == 128)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<float, 128, false, true>), grid, dim3(kWideThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<float, 64, false, true>), grid, dim3(kWideThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -38,10 +38,29 @@ struct FwdParams {
     float* nq_saved;     // [T,H] or nullptr
     float* nk_saved;     // [T,H] or nullptr
     float* u_saved;      // [slots,H,64,dv] fp32: U of every chunk (bf16 inputs), or nullptr
+    const int32_t* sf_dst;   // per sequence: row of sfinal to write, or -1 to skip; nullptr = itself
     int64_t T;
     int32_t N, H, dv, seqlen;
     float eps, scale;
-    int32_t nslices;     // dv / kSlice
+    int32_t nslices;     // dv / kSlice (segment maps: (dk + dv) / kSlice)
+    int32_t map_slices;  // segment maps: the first dk / kSlice slices carry M, the rest B
+};
+
+// Segment split of long sequences for the two-level forward (bf16 inputs).
+struct SegParams {
+    const int32_t* cu;   // documents [N+1] (device) or nullptr: N equal sequences of seqlen
+    int32_t* seg_cu;     // [P+1] segment token bounds; unused trailing segments are empty at T
+    int32_t* doc_seg;    // [N+1] first segment of every document (doc_seg[N] = segments used)
+    int32_t* sf_dst;     // [P] document whose final state segment j ends, or -1
+    int64_t T;
+    int32_t N, seqlen, seg_len, P;
+};
+struct CarryParams {
+    const int32_t* doc_seg;
+    const float* s0;     // [N,H,dk,dv] or nullptr
+    const float* maps;   // [P,H,dk,dk+dv]: [M | B] of every segment
+    float* s_in;         // [P,H,dk,dv]: the state entering every segment
+    int32_t N, H, dv, nslices;
 };
 
 struct BwdParams {
@@ -92,5 +111,9 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int dk, b
 constexpr int kBwdScan = 1, kBwdGrads = 2;
 hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int in_dtype, int out_dtype, int dk, hipStream_t stream);
+// Two-level forward pieces (bf16 inputs): segment split, segment maps, carry scan.
+hipError_t launch_segments(const SegParams& p, hipStream_t stream);
+hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t stream);
+hipError_t launch_carry(const CarryParams& p, int dk, hipStream_t stream);
 
 }  // namespace kda

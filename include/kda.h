@@ -75,6 +75,7 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /* kda_config.flags */
 #define KDA_FLAG_SAVE_FOR_BWD 1u /* forward also fills `saved` for kda_bwd */
+#define KDA_FLAG_SEQUENTIAL 2u   /* forward: never split long sequences into segments */
 
 typedef struct kda_config {
     int32_t H;         /* heads                                        */
@@ -97,7 +98,8 @@ void kda_config_init(kda_config* cfg, int32_t H, int32_t dk, int32_t dv);
  * and, for bf16 inputs, each chunk's pseudo-values U = T beta v - W S (fp32).
  * kda_fwd_workspace_size / kda_bwd_workspace_size: scratch for one call (the
  * backward's holds dL/dS at the end of every chunk and, for bf16 inputs, each
- * chunk's dL/dU). */
+ * chunk's dL/dU; the forward's is non-zero only when it splits long sequences,
+ * see kda_fwd). */
 size_t kda_saved_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
@@ -107,7 +109,19 @@ size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32
  * own entry, never from the previous document).  final_state: fp32
  * [num_seqs, H, dk, dv] or NULL.  saved: required (kda_saved_size bytes) iff
  * flags has KDA_FLAG_SAVE_FOR_BWD, else ignored.  workspace may be NULL when
- * kda_fwd_workspace_size() is 0. */
+ * kda_fwd_workspace_size() is 0.
+ *
+ * Long sequences.  With bf16 inputs, no KDA_FLAG_SAVE_FOR_BWD and no
+ * KDA_FLAG_SEQUENTIAL, when there are few (sequence, head) chains for the
+ * GPU and the documents are long (the test is on cfg, total_tokens and
+ * num_seqs only), every document is cut into segments: each segment's affine
+ * map S_out = M S_in + B is computed in parallel, the maps are composed per
+ * document in fp32, and the segments are rerun from their entering states.
+ * The chunk boundaries do not move, so only rounding differs from the
+ * one-pass forward.  The workspace (kda_fwd_workspace_size bytes) then holds
+ * the segment bounds, the maps and the entering states ("Large models on
+ * Ascend: from adaptation challenges to efficient training", ruibaoantu.com
+ * 9569846, section 2: the KDA recurrence spread over many compute units). */
 kda_status kda_fwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
                    const void* k, const void* v, const void* g, const void* beta,
                    const int32_t* cu_seqlens, const float* initial_state, void* o,

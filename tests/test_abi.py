@@ -153,3 +153,27 @@ def test_decode_rejects_bad_arguments():
     # nothing to do: returns before any HIP call
     cfg.in_dtype = KDA_F32
     assert _decode(cfg, N=0, q=0, s_out=0, o=0) == KDA_OK
+
+
+def test_fwd_workspace_for_long_sequences():
+    """The forward needs a workspace only when it splits long sequences: bf16
+    inputs, few (sequence, head) chains, long documents, no state save and no
+    KDA_FLAG_SEQUENTIAL."""
+    long_cfg = _lib.make_config(16, 128, 128, KDA_BF16, KDA_F32)
+    ws = _lib.kda_fwd_workspace_size(long_cfg, 1 << 20, 1)
+    # at least the maps [M | B] (dk x (dk + dv)) and entering states of two segments per head
+    assert ws >= 2 * 16 * 128 * (256 + 128) * 4
+    assert _lib.kda_fwd_workspace_size(long_cfg, 4 * 8192, 4) == 0          # 256 chains fill the GPU
+    assert _lib.kda_fwd_workspace_size(long_cfg, 4096, 1) == 0              # too short to split
+    seq = _lib.make_config(16, 128, 128, KDA_BF16, KDA_F32, flags=_lib.KDA_FLAG_SEQUENTIAL)
+    assert _lib.kda_fwd_workspace_size(seq, 1 << 20, 1) == 0
+    save = _lib.make_config(16, 128, 128, KDA_BF16, KDA_F32, flags=KDA_FLAG_SAVE_FOR_BWD)
+    assert _lib.kda_fwd_workspace_size(save, 1 << 20, 1) == 0
+    f32 = _lib.make_config(2, 64, 64, KDA_F32, KDA_F32)
+    assert _lib.kda_fwd_workspace_size(f32, 1 << 20, 1) == 0
+    # too small or missing workspace is refused before any launch
+    assert _fwd(long_cfg, T=1 << 20, ws=FAKE, wsb=ws - 1) == KDA_ERR_WORKSPACE
+    assert _fwd(long_cfg, T=1 << 20, ws=0, wsb=ws) == KDA_ERR_INVALID_ARG and "workspace" in _err()
+    cfg = _lib.make_config(2, 64, 64, KDA_BF16)
+    cfg.flags = 4
+    assert _fwd(cfg) == KDA_ERR_INVALID_ARG
