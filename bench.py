@@ -26,6 +26,14 @@ implementation saves or recomputes is not counted), per kernel:
 
 `decode` reports the serving step on its own: 256 sequences x 32 heads, d = 128,
 bf16 token inputs, the fp32 state updated in place, one token per call.
+
+`long_context` reports the inference forward on one 1,048,576-token sequence x
+16 heads (d = 128, bf16), which takes the library's two-level path, next to
+the one-pass forward on the same inputs.  Its inputs are drawn on the device
+with a seeded torch generator in the workload's distributions (q, k, v, beta
+logit ~ N(0, 1); g = -softplus(N(-2, 1)); initial state ~ N(0, 0.01)), since
+drawing 2^31 values per tensor on the host takes minutes.  Its parity against
+the oracle is a test case (the same shape, host-drawn inputs).
 """
 import argparse
 import json
@@ -274,6 +282,26 @@ def main():
     dec_bytes = decode_bytes(DECODE_N, H, dk, dv)
     del sd
 
+    # one long sequence: the two-level forward, and the one-pass forward beside it
+    lc_T, lc_H = 1 << 20, 16
+    gen = torch.Generator(device=dev).manual_seed(1003)
+    lq, lk, lv = (torch.randn(lc_T, lc_H, dk, device=dev, generator=gen).bfloat16() for _ in range(3))
+    lg = (-torch.nn.functional.softplus(torch.randn(lc_T, lc_H, dk, device=dev, generator=gen) - 2.0)).bfloat16()
+    lb = torch.randn(lc_T, lc_H, device=dev, generator=gen).bfloat16()
+    ls0 = 0.1 * torch.randn(1, lc_H, dk, dv, device=dev, generator=gen)
+    lc_ms = {}
+    for mode in ("split", "one_pass"):
+        seq = mode == "one_pass"
+        kda.kda_fwd(lq, lk, lv, lg, lb, None, ls0, sequential=seq)
+        e0.record(stream)
+        for _ in range(3):
+            kda.kda_fwd(lq, lk, lv, lg, lb, None, ls0, sequential=seq)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lc_ms[mode] = e0.elapsed_time(e1) / 3
+    lc_bytes = alg_bytes(1, lc_T, lc_H, dk, dv, "fwd")
+    del lq, lk, lv, lg, lb, ls0
+
     tokens = B * T
     names = {"fwd": "kda_fwd_bf16_kernel (training forward, state save)",
              "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
@@ -316,6 +344,13 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                 "traffic": traffic_record("decode"), "alg_bytes_per_launch": dec_bytes}},
+        "long_context": {"workload": f"kda-fwd-bf16-B1-H{lc_H}-T{lc_T}-d{dk} (inference, two-level)",
+                         "ms": lc_ms["split"], "tokens_per_s": lc_T / (lc_ms["split"] * 1e-3),
+                         "one_pass_ms": lc_ms["one_pass"],
+                         "roofline": {"bound": "hbm", "achieved": lc_bytes / (lc_ms["split"] * 1e-3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": lc_bytes / (lc_ms["split"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "alg_bytes_per_call": lc_bytes}},
         "timed_wall_s": wall,
     }
     if args.copy_probe_mib > 0:
