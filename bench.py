@@ -83,12 +83,16 @@ def decode_bytes(N, H, dk, dv):
     return N * H * (2 * dk * dv * 4 + (3 * dk + dv + 1) * 2 + dv * 4)
 
 
-KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file)
-    "grads": ("kda_bwd_grads_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
-    "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip"),
-    "fwd": ("kda_fwd_bf16_kernel<float, 128, true>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
-    "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip"),
-    "decode": ("kda_decode_kernel", "gated_delta_rule_41_amd/csrc/kda_decode.hip"),
+FWD_GRID = 4 * 32 * 2 * 512   # threads in one launch of the workload's fused forward (one per chain and slice)
+
+KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file, grid size or None)
+    "grads": ("kda_bwd_grads_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
+    "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
+    "fwd": ("kda_fwd_bf16_kernel<float, 128, true, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip", FWD_GRID),
+    # the long-context run's second level launches the same kernel on another grid
+    "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip",
+                  FWD_GRID),
+    "decode": ("kda_decode_kernel", "gated_delta_rule_41_amd/csrc/kda_decode.hip", None),
 }
 
 
@@ -106,7 +110,7 @@ def pmc_summary(fetch_csv, write_csv, probe_mib):
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
                     sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
         return sums
 
@@ -118,8 +122,8 @@ def pmc_summary(fetch_csv, write_csv, probe_mib):
         scale[counter] = probe_bytes / (sums[last] * 1024.0)
         rec.setdefault("_probe", {"bytes_read": probe_bytes, "bytes_written": probe_bytes})[counter] = {
             "kernel": last[1][:100], "kib": sums[last], "scale": scale[counter]}
-        for key, (needle, src) in KERNELS.items():
-            vals = [v for (_, name), v in sums.items() if needle in name]
+        for key, (needle, src, grid) in KERNELS.items():
+            vals = [v for (_, name, gs), v in sums.items() if needle in name and (grid is None or gs == grid)]
             if vals:
                 rec.setdefault(key, {"kernel": needle, "source": src, "dispatches": len(vals)})[counter + "_kib"] = \
                     sum(vals) / len(vals)

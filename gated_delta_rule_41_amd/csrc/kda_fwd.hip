@@ -545,7 +545,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (r0 + i < L) {
-                rq[i].load(qc + (ok + i * sk));
+                if (MAP) rq[i].zero();   // the maps need no queries
+                else rq[i].load(qc + (ok + i * sk));
                 rk[i].load(kc + (ok + i * sk));
                 rg[i].load(gc + (ok + i * sk));
                 if (!is_state) {
@@ -642,8 +643,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 kih[e] = from_f32<T>(vi[e]);
                 xkil[i][e] = from_f32<T>(vi[e] - to_f32(kih[e]));
             }
-            *reinterpret_cast<VH*>(&sm.qg[r * PK + pc0]) = qh;
-            *reinterpret_cast<VH*>(&sm.qgl[r * PK + pc0]) = ql;
+            if (!MAP) {
+                *reinterpret_cast<VH*>(&sm.qg[r * PK + pc0]) = qh;
+                *reinterpret_cast<VH*>(&sm.qgl[r * PK + pc0]) = ql;
+            }
             *reinterpret_cast<VH*>(&sm.kg[r * PK + pc0]) = kg;
             *reinterpret_cast<VH*>(&sm.ki[r * PK + pc0]) = kih;
         }
@@ -712,17 +715,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             for (int kk = 0; kk < NKB; ++kk) {
                 const V8T bh = lds8<T>(sm.ki + rbk + 32 * kk);
                 akk = mma_k32(akk, lds8<T>(sm.kg + ra + 32 * kk), bh);
-                aqk = mma3<true>(aqk, lds8<T>(sm.qg + ra + 32 * kk), lds8<T>(sm.qgl + ra + 32 * kk), bh,
-                                 lds8<T>(sm.kil + rbk + 32 * kk));
+                if (!MAP)
+                    aqk = mma3<true>(aqk, lds8<T>(sm.qg + ra + 32 * kk), lds8<T>(sm.qgl + ra + 32 * kk), bh,
+                                     lds8<T>(sm.kil + rbk + 32 * kk));
             }
             const int s = 16 * jb + cl;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * ib + 4 * qg + i;
-                const float vq = s <= r ? aqk[i] : 0.f;
-                const T hi = from_f32<T>(vq);
-                sm.aqk[r * PC + perm32(s)] = hi;
-                sm.aqkl[r * PC + perm32(s)] = from_f32<T>(vq - to_f32(hi));
+                if (!MAP) {
+                    const float vq = s <= r ? aqk[i] : 0.f;
+                    const T hi = from_f32<T>(vq);
+                    sm.aqk[r * PC + perm32(s)] = hi;
+                    sm.aqkl[r * PC + perm32(s)] = from_f32<T>(vq - to_f32(hi));
+                }
                 const float vk = s < r ? akk[i] : 0.f;
                 sm.akk[r * PC + s] = from_f32<T>(vk);
                 if (ib == jb) sm.adiag[ib][4 * qg + i][cl] = vk;
