@@ -963,6 +963,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const T* __restrict__ bc = reinterpret_cast<const T*>(p.b) + c0 * H + h;
     const float* __restrict__ S0 = reinterpret_cast<const float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
     const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
+    float xs0[NKV][8], xd0[NKV][8];   // S0 / dS1 row fragments (loaded before Akk)
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const int r0 = 16 * wl + 4 * qg;             // prep layout: rows r0..r0+3
@@ -1100,6 +1101,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     put_rm(P, S(4), S(4), vKG, false);   // KG  h
     lds_barrier();
 
+    // S0 / dS1 row fragments of key column block 16w for dQG, dW and dKtil,
+    // issued here so that their latency hides under Akk, T and the staging
+    if (kact) {
+        const int nr = 16 * w + cl;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            gf8(xs0[kk], S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            gf8(xd0[kk], dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+        }
+    }
     // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
     if (w < 4) {
@@ -1189,17 +1200,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     }
     lds_barrier();
 
-    // S0 / dS1 row fragments of key column block 16w, issued before dBV and
-    // dAqk so their latency hides under those products
-    float xs0[NKV][8], xd0[NKV][8];
-    if (kact) {
-        const int nr = 16 * w + cl;
-#pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) {
-            gf8(xs0[kk], S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-            gf8(xd0[kk], dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-        }
-    }
     // ================= dBV = T^T dU  ->  dv, dbeta (v part) =================
     float dbv_part[4][4];   // this wave's share of sum_j v dBV per row (waves 4-7 add theirs later)
     if (vact) {
