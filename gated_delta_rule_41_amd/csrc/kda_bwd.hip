@@ -978,25 +978,33 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         RawRow<T, CPH> q[4], k[4];
         float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4];
     };
-    auto prep_fill = [&](Prep& P, bool first) {
+    // after_loads runs once the row loads are issued, before their first use:
+    // more loads issued there wait only behind these
+    auto prep_fill = [&](Prep& P, bool first, auto after_loads) {
         RawRow<T, CPH> rg[4];
+        float rb[4], nq[4], nk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            float rb = 0.f, nq = 1.f, nk = 1.f;
+            rb[i] = 0.f; nq[i] = 1.f; nk[i] = 1.f;
             if (r < L) {
                 P.q[i].load(qc + r * rsk + ck0);
                 P.k[i].load(kc + r * rsk + ck0);
                 rg[i].load(gcp + r * rsk + ck0);
-                rb = gload1(bc + (int64_t)r * H);
-                nq = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
-                nk = p.nk_saved[(c0 + r) * H + h];
+                rb[i] = gload1(bc + (int64_t)r * H);
+                nq[i] = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
+                nk[i] = p.nk_saved[(c0 + r) * H + h];
             } else {
                 P.q[i].zero(); P.k[i].zero(); rg[i].zero();
             }
-            P.beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb)) : 0.f;
-            P.iq[i] = p.scale / nq;
-            P.ik[i] = 1.f / nk;
+        }
+        after_loads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            P.beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
+            P.iq[i] = p.scale / nq[i];
+            P.ik[i] = 1.f / nk[i];
         }
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
@@ -1070,25 +1078,26 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     RawRow<T, VPH> ddr[4], vvr[4];   // dO and v rows of this lane (prep layout), staged in LDS later
     {
     Prep P;
-    prep_fill(P, true);
-    if (vact) {
-        const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
-        const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
+    prep_fill(P, true, [&]() {
+        if (vact) {
+            const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
+            const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * w + cl;
-                U[mb][i] = ub[o];
-                dU[mb][i] = dub[o];
-            }
-    }
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * w + cl;
+                    U[mb][i] = ub[o];
+                    dU[mb][i] = dub[o];
+                }
+        }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        if (r < L) { vvr[i].load(vc + r * rsv + cv0); ddr[i].load(doc + r * rsv + cv0); }
-        else { vvr[i].zero(); ddr[i].zero(); }
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            if (r < L) { vvr[i].load(vc + r * rsv + cv0); ddr[i].load(doc + r * rsv + cv0); }
+            else { vvr[i].zero(); ddr[i].zero(); }
+        }
+    });
     if (wl == 0 && qg == 0) {
 #pragma unroll
         for (int e = 0; e < CPH; ++e) sgc[ck0 + e] = fast_exp2(P.GC[e]);
@@ -1310,7 +1319,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     }
     {
     Prep P;
-    prep_fill(P, false);
+    prep_fill(P, false, [] {});
     // dW rm (slot 2), KG rm (slot 6)
     if (kact) {
 #pragma unroll
@@ -1443,7 +1452,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 
     // ================= chain rule to qh, kh, beta, G =================
     Prep P;
-    prep_fill(P, false);
+    prep_fill(P, false, [] {});
     float dqh[4][CPH], dkh[4][CPH], dG[4][CPH], dbk[4], colp[CPH];
 #pragma unroll
     for (int e = 0; e < CPH; ++e) colp[e] = 0.f;

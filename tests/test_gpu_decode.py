@@ -71,9 +71,9 @@ def test_decode_zero_state_and_bf16_output():
     torch.cuda.synchronize()
     assert o.dtype == torch.bfloat16
     o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=np.arange(N + 1))
-    # storing o in bf16 adds up to 2^-9 |o| (round to nearest); the compute
+    # storing o in bf16 adds up to 2^-8 |o| (round to nearest, 8-bit significand); the compute
     # error on top of that storage rounding is held to the bf16 bar
-    excess = np.abs(host(o) - o_ref) - 2.0 ** -9 * np.abs(o_ref)
+    excess = np.abs(host(o) - o_ref) - 2.0 ** -8 * np.abs(o_ref)
     err = excess.max() / np.sqrt(np.mean(o_ref ** 2))
     e2 = frob_rel(host(s1), s_ref)
     _say(f"zero state: o excess over bf16 rounding {err:.2e}, state frob {e2:.2e}")

@@ -65,9 +65,9 @@ def test_ragged_varlen_small(dtype, dk, dv):
         o, sf, *_ = run_fwd(x, dtype, cu=cu, out_dtype=out_dtype)
         o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"])
         if out_dtype == torch.bfloat16:
-            # storing o in bf16 adds up to 2^-9 |o| (round to nearest); the compute
+            # storing o in bf16 adds up to 2^-8 |o| (round to nearest, 8-bit significand); the compute
             # error on top of that storage rounding is held to the bf16 bar
-            excess = np.abs(host(o) - o_ref) - 2.0 ** -9 * np.abs(o_ref)
+            excess = np.abs(host(o) - o_ref) - 2.0 ** -8 * np.abs(o_ref)
             err = excess.max() / np.sqrt(np.mean(o_ref ** 2))
             assert err <= 2e-2, err
         else:
