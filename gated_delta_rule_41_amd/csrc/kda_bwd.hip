@@ -404,7 +404,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     typedef bf16x8 V8T;
     typedef bf16x4 V4T;
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
+    const int tid = threadIdx.x, w = tid >> 6;
+    // Lane coordinates, re-derived at the top of every step from a lane index
+    // the optimiser cannot see through, so lane-dependent addresses and masks
+    // are recomputed per step instead of being held across the loop.
+    int l = tid & 63, qg = l >> 4, cl = l & 15;
     const bool is_state = w < 4;
     const int ww = w & 3;
     int chain, slice;
@@ -414,7 +418,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
     const int dv = p.dv, H = p.H;
     const int dv0 = slice * kSlice;
-    const int vcol = dv0 + 16 * ww + cl;
+    int vcol = dv0 + 16 * ww + cl;
+    auto refresh = [&]() {
+        asm volatile("" : "+v"(l));
+        qg = l >> 4;
+        cl = l & 15;
+        vcol = dv0 + 16 * ww + cl;
+    };
     const int64_t nchunks = (t1 - t0 + kChunk - 1) / kChunk;
 
     const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
@@ -430,11 +440,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     RawScalar<T> rb[4];
     float nq[4], nk[4], beta[4];
     int Lp = 0;
+    // second buffer: the chunk after the one being prepared, loaded early in a
+    // step so that the address unit works under the LDS steps instead of
+    // stalling the end of the chunk
+    RawRow<T, CPL> nrq[4], nrk[4], nrg[4];
+    RawRow<T, VPL> nrdo[4];
+    RawScalar<T> nrb[4];
+    int nLp = 0;
     V4T xqh[4][CQ], xql[4][CQ];   // qh Gam hi/lo of the chunk to run next
     RawRow<T, VPL> xdo[4];        // its dO slice
     float xgc[CPL];               // its Gam_C
 
-    auto load_chunk = [&](int64_t c0) {
+    auto load_rows = [&](int64_t c0, RawRow<T, CPL> (&xq)[4], RawRow<T, CPL> (&xk)[4], RawRow<T, CPL> (&xg)[4],
+                         RawRow<T, VPL> (&xd)[4], RawScalar<T> (&xb)[4], int& xl) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
         const int r0 = 16 * ww + 4 * qg;
         const T* qc = qp + (c0 + r0) * rs_k + h * DK + CPL * cl;
@@ -445,22 +463,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (r0 + i < L) {
-                rq[i].load(qc + i * rs_k);
-                rk[i].load(kc + i * rs_k);
-                rg[i].load(gc + i * rs_k);
-                rdo[i].load(dc + i * rs_v);
-                rb[i].load(bc + i * H);
+                xq[i].load(qc + i * rs_k);
+                xk[i].load(kc + i * rs_k);
+                xg[i].load(gc + i * rs_k);
+                xd[i].load(dc + i * rs_v);
+                xb[i].load(bc + i * H);
             } else {
-                rq[i].zero(); rk[i].zero(); rg[i].zero(); rdo[i].zero();
-                rb[i].zero();
+                xq[i].zero(); xk[i].zero(); xg[i].zero(); xd[i].zero();
+                xb[i].zero();
             }
         }
-        Lp = L;
+        xl = L;
     };
-    V4T ltri;
+    auto load_chunk = [&](int64_t c0) { load_rows(c0, rq, rk, rg, rdo, rb, Lp); };
+    auto load_next = [&](int64_t c0) { load_rows(c0, nrq, nrk, nrg, nrdo, nrb, nLp); };
+    auto take_next = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
+        for (int i = 0; i < 4; ++i) {
+            rq[i] = nrq[i]; rk[i] = nrk[i]; rg[i] = nrg[i]; rdo[i] = nrdo[i]; rb[i] = nrb[i];
+        }
+        Lp = nLp;
+    };
     auto gate_prefix = [&](int e) {
+        V4T ltri;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
         const V4T b = __builtin_bit_cast(V4T, u16x4{rg[0].x[e], rg[1].x[e], rg[2].x[e], rg[3].x[e]});
         return mma_k16(f32x4{0.f, 0.f, 0.f, 0.f}, ltri, b);
     };
@@ -541,6 +568,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
         sm.aqt[e] = from_f32<T>(0.f);    // Aqk^T blocks above the diagonal are never written
         sm.aqtl[e] = from_f32<T>(0.f);
     }
+    // step 3 (both groups, two of the four rows each): Ktil = (kh/Gam) Gam_C in
+    // place of kh/Gam, in the prep layout (rows 16ww+4qg+i, key columns
+    // CPL*cl..), Gam_C from LDS
+    auto ktil_in_place = [&](int i0) {
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i) {
+            const int r = 16 * ww + 4 * qg + i;
+#pragma unroll
+            for (int e4 = 0; e4 < CQ; ++e4) {
+                const int c = CPL * cl + 4 * e4;
+                const int pc = perm32(c);
+                f32x4 x = lds4f<T>(&sm.r2[r * PK + pc]) + lds4f<T>(&sm.r3[r * PK + pc]);
+                x *= *reinterpret_cast<const f32x4*>(&sm.gc[c]);
+                sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], x);
+            }
+        }
+    };
     // step 2, shared: Akk and Aqk^T, one lower-triangle block pair per item
     auto intra_products = [&]() {
 #pragma unroll 1
@@ -609,6 +653,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
         for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
             const int64_t slot = t0 / kChunk + n + jc;
             // 1: dL/dS at the end of this chunk, for the chunk-parallel gradients
+            refresh();
             {
                 float* out = dst + (slot * H + h) * (int64_t)DK * dv;
 #pragma unroll
@@ -617,9 +662,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     for (int i = 0; i < 4; ++i) out[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
             }
             lds_barrier();
+            refresh();
             intra_products();
             lds_barrier();
-            // 3: (I + Akk_bb)^{-1}, block b = this wave
+            // 3: (I + Akk_bb)^{-1}, block b = this wave; Ktil in place
+            refresh();
             {
                 const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
                 f32x4 nbv;
@@ -629,10 +676,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
             }
+            ktil_in_place(0);
             lds_barrier();
+            refresh();
             w_solve();
             lds_barrier();
             // 5a: dU = Aqk^T dO + Ktil dS1
+            refresh();
             V8T dof[2], duf[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + (16 * ww + cl) * PC + 32 * kk + 8 * qg);
@@ -668,6 +718,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             }
             lds_barrier();
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
+            refresh();
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
@@ -702,6 +753,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
         for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
             const int64_t c0 = t0 + jc * kChunk;
             // 1: the tiles held in registers
+            refresh();
             {
                 const int pr = perm32(16 * ww + 4 * qg);
 #pragma unroll
@@ -725,10 +777,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 }
             }
             lds_barrier();
+            refresh();
+            if (jc > 1) load_next(c0 - 2 * kChunk);   // rows of the chunk before the previous one
             intra_products();
             lds_barrier();
-            // 3: (qh Gam)^T hi/lo over the qh Gam tiles (swizzled layout); Ktil = (kh/Gam) Gam_C
-            // in place of kh/Gam (each lane rewrites its own elements)
+            // 3: (qh Gam)^T hi/lo over the qh Gam tiles (swizzled layout); half of Ktil
+            refresh();
             {
                 const int pr = perm32(16 * ww + 4 * qg);
 #pragma unroll
@@ -745,29 +799,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                             pack4<T>(f32x4{lv[0][j], lv[1][j], lv[2][j], lv[3][j]});
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * ww + 4 * qg + i;
-#pragma unroll
-                    for (int e4 = 0; e4 < CQ; ++e4) {
-                        const int pc = perm32(CPL * cl + 4 * e4);
-                        f32x4 x = lds4f<T>(&sm.r2[r * PK + pc]) + lds4f<T>(&sm.r3[r * PK + pc]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) x[j] *= xgc[4 * e4 + j];
-                        sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], x);
-                    }
-                }
             }
+            ktil_in_place(2);
             lds_barrier();
+            refresh();
             w_solve();
             lds_barrier();
             // 5a: norms, sigmoid and gate sums of the previous chunk
+            refresh();
             if (jc > 0) prep_a();
             lds_barrier();
-            // 5b: its operand values; loads of the one before it
+            // 5b: its operand values; the rows loaded in step 2 become the next ones prepared
+            refresh();
             if (jc > 0) {
                 prep_b();
-                if (jc > 1) load_chunk(c0 - 2 * kChunk);
+                if (jc > 1) take_next();
             }
             lds_barrier();
         }
