@@ -29,6 +29,7 @@
 //          the blocked solve gives wave w the columns it owns.
 //   inter  wave w owns value columns 16w..16w+15 of the slice: its state
 //          columns, U columns and O columns stay in its registers.
+#include <cstddef>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -62,6 +63,13 @@ struct __attribute__((aligned(32))) FwdSmem {
     float gc[DK];             // Gam_C
     float red[4][DK];         // per-wave column sums of g
 };
+
+// Row stride (floats) of a state wave's 64 x 16 O patch staged for the stores
+// (rows 16-byte aligned).  Two patches fit in the Akk tile and two in the
+// diagonal-block arrays.
+constexpr int kOStride = 16;
+static_assert(2 * kChunk * kOStride * 4 <= kChunk * (kChunk + 8) * 2, "O patches exceed the Akk tile");
+static_assert(2 * kChunk * kOStride * 4 <= 2 * 4 * 16 * 20 * 4, "O patches exceed the diagonal-block arrays");
 
 template <typename T, typename TO, int DK, bool SAVE>
 __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
@@ -879,10 +887,29 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 for (int kk = 0; kk <= (i >> 1); ++kk)
                     O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + ra + 32 * kk), lds8<T>(sm.aqkl + ra + 32 * kk), ufh[kk],
                                       ufl[kk]);
+            }
+            if (!MAP) {
+                // O goes out through this wave's own patch of LDS that no step
+                // uses now (the Akk tile, the diagonal blocks), so that each lane
+                // writes 4 contiguous columns: four 16-byte stores per lane
+                // instead of sixteen 4-byte ones.  Only this wave touches its
+                // patch, and a wave's LDS operations complete in order.
+                static_assert(offsetof(SM, tdiag) == offsetof(SM, adiag) + sizeof(sm.adiag) &&
+                                  offsetof(SM, akk) % 16 == 0 && offsetof(SM, adiag) % 16 == 0,
+                              "the O patches need adiag/tdiag adjacent and 16-byte aligned tiles");
+                char* const patch = ww < 2 ? reinterpret_cast<char*>(sm.akk) : reinterpret_cast<char*>(sm.adiag);
+                float* ot = reinterpret_cast<float*>(patch) + (ww & 1) * kChunk * kOStride;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * i + 4 * qg + j;
-                    if (!MAP && r < L) op[((c0 + r) * H + h) * dv + vcol] = from_f32<TO>(O[i][j]);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ot[(16 * i + 4 * qg + j) * kOStride + cl] = O[i][j];
+                const int cg = l & 3, rr = l >> 2;
+                TO* ob = op + h * dv + dv0 + 16 * ww + 4 * cg;
+#pragma unroll
+                for (int pass = 0; pass < 4; ++pass) {
+                    const int r = 16 * pass + rr;
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * kOStride + 4 * cg]);
+                    if (r < L) sts4<TO>(ob + (c0 + r) * rs_v, x);
                 }
             }
 #pragma unroll
