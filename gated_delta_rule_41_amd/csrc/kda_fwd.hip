@@ -769,6 +769,34 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             for (int j = 0; j < 4; ++j) sm.ki[(16 * i + 4 * qg + j) * PK + pc] = from_f32<T>(-X[i][j]);
     };
 
+    // A state wave writes a 64 x 16 fp32 accumulator block (rows 16i+4qg+j,
+    // column cl of its 16 columns) to rows 0..nrows-1 of a row-major array
+    // (row stride ld elements; dst = row 0, the wave's first column) through
+    // its own patch of LDS that no step uses when this runs (the Akk tile, the
+    // diagonal-block arrays), so that each lane stores 4 contiguous columns:
+    // four 16-byte stores per lane instead of sixteen 4-byte ones.  Only the
+    // wave touches its patch, and a wave's LDS operations complete in order.
+    // (Used for o; the fp32 saves for the backward measured no faster this way.)
+    static_assert(offsetof(SM, tdiag) == offsetof(SM, adiag) + sizeof(sm.adiag) && offsetof(SM, akk) % 16 == 0 &&
+                      offsetof(SM, adiag) % 16 == 0,
+                  "the store patches need adiag/tdiag adjacent and 16-byte aligned tiles");
+    auto patch_out = [&](auto* dst, int64_t ld, const f32x4 (&blk)[4], int nrows) {
+        char* const patch = ww < 2 ? reinterpret_cast<char*>(sm.akk) : reinterpret_cast<char*>(sm.adiag);
+        float* ot = reinterpret_cast<float*>(patch) + (ww & 1) * kChunk * kOStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ot[(16 * i + 4 * qg + j) * kOStride + cl] = blk[i][j];
+        const int cg = l & 3, rr = l >> 2;
+        typedef typename std::remove_pointer<decltype(dst)>::type E;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int r = 16 * pass + rr;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * kOStride + 4 * cg]);
+            if (r < nrows) sts4<E>(dst + r * ld + 4 * cg, x);
+        }
+    };
+
     // Prologue: both groups prepare the first chunk.  Then the two groups run
     // separate loops with the same barrier sequence: six barriers per chunk.
     if (t0 < t1) {
@@ -888,30 +916,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                     O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + ra + 32 * kk), lds8<T>(sm.aqkl + ra + 32 * kk), ufh[kk],
                                       ufl[kk]);
             }
-            if (!MAP) {
-                // O goes out through this wave's own patch of LDS that no step
-                // uses now (the Akk tile, the diagonal blocks), so that each lane
-                // writes 4 contiguous columns: four 16-byte stores per lane
-                // instead of sixteen 4-byte ones.  Only this wave touches its
-                // patch, and a wave's LDS operations complete in order.
-                static_assert(offsetof(SM, tdiag) == offsetof(SM, adiag) + sizeof(sm.adiag) &&
-                                  offsetof(SM, akk) % 16 == 0 && offsetof(SM, adiag) % 16 == 0,
-                              "the O patches need adiag/tdiag adjacent and 16-byte aligned tiles");
-                char* const patch = ww < 2 ? reinterpret_cast<char*>(sm.akk) : reinterpret_cast<char*>(sm.adiag);
-                float* ot = reinterpret_cast<float*>(patch) + (ww & 1) * kChunk * kOStride;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ot[(16 * i + 4 * qg + j) * kOStride + cl] = O[i][j];
-                const int cg = l & 3, rr = l >> 2;
-                TO* ob = op + h * dv + dv0 + 16 * ww + 4 * cg;
-#pragma unroll
-                for (int pass = 0; pass < 4; ++pass) {
-                    const int r = 16 * pass + rr;
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * kOStride + 4 * cg]);
-                    if (r < L) sts4<TO>(ob + (c0 + r) * rs_v, x);
-                }
-            }
+            if (!MAP) patch_out(op + (c0 * H + h) * dv + dv0 + 16 * ww, rs_v, O, L);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
