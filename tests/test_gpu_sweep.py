@@ -1,0 +1,112 @@
+"""Seeded sweep of shapes against the fp64 oracle, through the C ABI.
+
+Each case draws document lengths (including empty, one-token, chunk-edge and
+ragged ones), head count, head dims, input dtype and whether there is an
+initial state from a fixed seed, then checks the forward (o, final state) and,
+where the shape allows training, the backward (all gradients) against the
+oracle with the bars in tests/gpu_util.py.  A few cases are long documents over
+few heads, which take the library's two-level forward.  Sizes keep the oracle
+to about a second per case.
+"""
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+
+from gpu_util import (BF16_FROB, BF16_MAX_RMS, F32_TOL, dev, frob_rel, host, inf_rel, max_over_rms, need_gpu,
+                      torch)
+
+import gated_delta_rule_41_amd as kda
+from gated_delta_rule_41_amd import _lib
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENGTHS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 191]
+
+
+def _say(msg):
+    print(f"[gpu-sweep] {msg}", flush=True)
+
+
+def _case(seed):
+    rng = np.random.default_rng([4242, seed])
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    dk = 64 if dtype == "f32" else int(rng.choice([64, 128]))
+    dv = int(rng.choice([64, 128]))
+    H = int(rng.integers(1, 5))
+    ndoc = int(rng.integers(1, 6))
+    lens = [int(rng.choice(EDGE_LENGTHS)) if rng.random() < 0.5 else int(rng.integers(1, 400)) for _ in range(ndoc)]
+    if sum(lens) == 0:
+        lens[0] = 70
+    with_s0 = bool(rng.random() < 0.7)
+    return dtype, dk, dv, H, lens, with_s0
+
+
+def _bar(dtype):
+    return (F32_TOL, F32_TOL) if dtype == "f32" else (BF16_MAX_RMS, BF16_FROB)
+
+
+def _err(dtype, a, r, state=False):
+    if dtype == "f32":
+        return inf_rel(a, r)
+    return frob_rel(a, r) if state else max_over_rms(a, r)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_forward_backward(seed):
+    need_gpu()
+    dtype, dk, dv, H, lens, with_s0 = _case(seed)
+    _say(f"seed {seed}: {dtype} dk={dk} dv={dv} H={H} lens={lens} s0={with_s0}")
+    cu = kda_inputs.cu_from_lengths(lens)
+    T = int(cu[-1])
+    x = kda_inputs.generate(500 + seed, T, H, dk, dv, dtype, num_seqs=len(lens), with_s0=with_s0, with_grads=True)
+    d = {k: dev(x[k], dtype) for k in ("q", "k", "v", "g", "b", "dO")}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0 = torch.from_numpy(x["s0"]).cuda() if with_s0 else None
+    dS = torch.from_numpy(x["dS"]).cuda()
+    o, sf, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, save_for_bwd=True)
+    gr = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS)
+    torch.cuda.synchronize()
+    o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu,
+                               initial_state=x["s0"] if with_s0 else None)
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["b"], x["dO"], cu_seqlens=cu,
+                     initial_state=x["s0"] if with_s0 else None, dS_final=x["dS"])
+    bar, sbar = _bar(dtype)
+    errs = {"o": _err(dtype, host(o), o_ref), "S_T": _err(dtype, host(sf), sf_ref, True)}
+    for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "db")):
+        errs[name] = _err(dtype, host(gr[name]), ref[rname])
+    errs["dS0"] = _err(dtype, host(gr["dS0"]), ref["dS0"], True)
+    _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert np.isfinite(v), k
+        assert v <= (sbar if k in ("S_T", "dS0") else bar), (k, v)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sweep_two_level_forward(seed):
+    """Long documents over few heads: the library splits them into segments."""
+    need_gpu()
+    rng = np.random.default_rng([4343, seed])
+    H = int(rng.integers(1, 3))
+    dk = int(rng.choice([64, 128]))
+    dv = int(rng.choice([64, 128]))
+    lens = [int(rng.integers(9000, 40000)) for _ in range(int(rng.integers(1, 3)))]
+    lens.insert(int(rng.integers(0, len(lens) + 1)), int(rng.choice([0, 1, 64, 65])))
+    cu = kda_inputs.cu_from_lengths(lens)
+    T = int(cu[-1])
+    cfg = _lib.make_config(H, dk, dv, _lib.KDA_BF16, _lib.KDA_F32)
+    assert _lib.kda_fwd_workspace_size(cfg, T, len(lens)) > 0, "expected the two-level path"
+    with_s0 = bool(rng.random() < 0.5)
+    _say(f"two-level seed {seed}: dk={dk} dv={dv} H={H} lens={lens} s0={with_s0}")
+    x = kda_inputs.generate(600 + seed, T, H, dk, dv, "bf16", num_seqs=len(lens), with_s0=with_s0)
+    d = {k: dev(x[k], "bf16") for k in ("q", "k", "v", "g", "b")}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0 = torch.from_numpy(x["s0"]).cuda() if with_s0 else None
+    o, sf, _ = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0)
+    torch.cuda.synchronize()
+    o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu,
+                               initial_state=x["s0"] if with_s0 else None)
+    e1, e2 = max_over_rms(host(o), o_ref), frob_rel(host(sf), sf_ref)
+    _say(f"  o max/rms {e1:.2e} S_T frob {e2:.2e}")
+    assert e1 <= BF16_MAX_RMS and e2 <= BF16_FROB
