@@ -66,6 +66,9 @@ kda_status check_sizes(const kda_config* c, int64_t T, int32_t N, const int32_t*
         return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is NULL but total_tokens is not a multiple of num_seqs%s");
     if ((int64_t)N * c->H * (c->dv / kda::kSlice) >= ((int64_t)1 << 31))
         return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large%s");
+    // the kernels address a chunk's rows with 32-bit offsets from a 64-bit base
+    if ((int64_t)kda::kChunk * c->H * (c->dk > c->dv ? c->dk : c->dv) >= ((int64_t)1 << 31))
+        return fail(KDA_ERR_UNSUPPORTED, "H too large%s");
     return KDA_OK;
 }
 

@@ -1001,6 +1001,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
 
     const int64_t rsk = (int64_t)H * DK, rsv = (int64_t)H * DV;   // token strides
+    // per-lane offsets inside a chunk fit in 32 bits (64 H max(dk, dv) < 2^31 is
+    // checked on the host); only the chunk bases are 64-bit
+    const int rk32 = (int)rsk, rv32 = (int)rsv;
+    const float* __restrict__ nqc = p.nq_saved + c0 * H + h;
+    const float* __restrict__ nkc = p.nk_saved + c0 * H + h;
     const T* __restrict__ qc = reinterpret_cast<const T*>(p.q) + c0 * rsk + h * DK;
     const T* __restrict__ kc = reinterpret_cast<const T*>(p.k) + c0 * rsk + h * DK;
     const T* __restrict__ gcp = reinterpret_cast<const T*>(p.g) + c0 * rsk + h * DK;
@@ -1034,12 +1039,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             const int r = r0 + i;
             rb[i] = 0.f; nq[i] = 1.f; nk[i] = 1.f;
             if (r < L) {
-                P.q[i].load(qc + r * rsk + ck0);
-                P.k[i].load(kc + r * rsk + ck0);
-                rg[i].load(gcp + r * rsk + ck0);
-                rb[i] = gload1(bc + (int64_t)r * H);
-                nq[i] = p.nq_saved[(c0 + r) * H + h];     // norms saved by the forward
-                nk[i] = p.nk_saved[(c0 + r) * H + h];
+                P.q[i].load(qc + (r * rk32 + ck0));
+                P.k[i].load(kc + (r * rk32 + ck0));
+                rg[i].load(gcp + (r * rk32 + ck0));
+                rb[i] = gload1(bc + r * H);
+                nq[i] = nqc[r * H];     // norms saved by the forward
+                nk[i] = nkc[r * H];
             } else {
                 P.q[i].zero(); P.k[i].zero(); rg[i].zero();
             }
@@ -1048,9 +1053,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            P.beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
-            P.iq[i] = p.scale / nq[i];
-            P.ik[i] = 1.f / nk[i];
+            // v_rcp (~1 ulp), as the forward forms beta and the reciprocal norms
+            P.beta[i] = (r < L) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
+            P.iq[i] = p.scale * __builtin_amdgcn_rcpf(nq[i]);
+            P.ik[i] = __builtin_amdgcn_rcpf(nk[i]);
         }
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
@@ -1132,7 +1138,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int64_t o = (int64_t)(16 * mb + 4 * qg + i) * DV + 16 * w + cl;
+                    const int o = (16 * mb + 4 * qg + i) * DV + 16 * w + cl;
                     U[mb][i] = ub[o];
                     dU[mb][i] = dub[o];
                 }
@@ -1140,7 +1146,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = r0 + i;
-            if (r < L) { vvr[i].load(vc + r * rsv + cv0); ddr[i].load(doc + r * rsv + cv0); }
+            if (r < L) { vvr[i].load(vc + (r * rv32 + cv0)); ddr[i].load(doc + (r * rv32 + cv0)); }
             else { vvr[i].zero(); ddr[i].zero(); }
         }
     });
@@ -1162,8 +1168,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         const int nr = 16 * w + cl;
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
-            gf8(xs0[kk], S0 + (int64_t)nr * DV + 32 * kk + 8 * qg);
-            gf8(xd0[kk], dS1 + (int64_t)nr * DV + 32 * kk + 8 * qg);
+            gf8(xs0[kk], S0 + (nr * DV + 32 * kk + 8 * qg));
+            gf8(xd0[kk], dS1 + (nr * DV + 32 * kk + 8 * qg));
         }
     }
     // ================= Akk (fp32 -> slot 5) =================
@@ -1281,7 +1287,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mb + 4 * qg + i;
                 if (r < L) {
-                    dvp[r * rsv + nc] = from_f32<TO>(sbeta[r] * a[i]);
+                    dvp[r * rv32 + nc] = from_f32<TO>(sbeta[r] * a[i]);
                     rowpart[mb][i] += to_f32(S(2)[r * PV + nc]) * a[i];
                 }
             }
@@ -1583,6 +1589,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     TO* __restrict__ dkp = reinterpret_cast<TO*>(p.dk) + c0 * rsk + h * DK;
     TO* __restrict__ dgp = reinterpret_cast<TO*>(p.dg) + c0 * rsk + h * DK;
     TO* __restrict__ dbp = reinterpret_cast<TO*>(p.db) + c0 * H + h;
+    const float isc2 = p.scale != 0.f ? 1.f / (p.scale * p.scale) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
@@ -1590,8 +1597,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             const float aq = P.iq[i], ai = P.ik[i];
             const float sq = srow[0 * 64 + r] + srow[3 * 64 + r];
             const float sk = srow[1 * 64 + r] + srow[4 * 64 + r];
-            const float sc = p.scale;
-            const float qdot = sc != 0.f ? sq / (sc * sc) : 0.f;   // (qh . dqh) / scale^2
+            const float qdot = sq * isc2;   // (qh . dqh) / scale^2
             float vq[CPH], vk[CPH];
 #pragma unroll
             for (int e = 0; e < CPH; ++e) {
@@ -1599,14 +1605,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 vq[e] = aq * (dqh[i][e] - qh * qdot);
                 vk[e] = ai * (dkh[i][e] - kh * sk);
             }
-            const int64_t off = r * rsk + ck0;
+            const int off = r * rk32 + ck0;
             store_row<TO, CPH>(dqp + off, vq);
             store_row<TO, CPH>(dkp + off, vk);
             store_row<TO, CPH>(dgp + off, dG[i]);
             if (wh == 0 && cl == 0) {
                 const float db = srow[2 * 64 + r] + srow[5 * 64 + r];
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
-                dbp[(int64_t)r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
+                dbp[r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
             }
         }
     }

@@ -49,7 +49,9 @@
  *    undefined behaviour; the kernels clamp every document to
  *    [0, total_tokens) so it cannot address memory outside the buffers.
  *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
- *    {KDA_F32, KDA_BF16}; H >= 1; total_tokens < 2^31; per-chunk cumulative
+ *    {KDA_F32, KDA_BF16}; H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
+ *    kernels address a chunk's rows with 32-bit offsets; KDA_ERR_UNSUPPORTED
+ *    otherwise); total_tokens < 2^31; per-chunk cumulative
  *    log-decay sum_{chunk} g >= -80 per channel (the kernels factor
  *    exp(G_r - G_s) = exp(G_r) exp(-G_s) inside a 64-token chunk).
  */

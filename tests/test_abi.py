@@ -177,3 +177,9 @@ def test_fwd_workspace_for_long_sequences():
     cfg = _lib.make_config(2, 64, 64, KDA_BF16)
     cfg.flags = 4
     assert _fwd(cfg) == KDA_ERR_INVALID_ARG
+
+
+def test_head_count_bound():
+    """64 * H * max(dk, dv) must stay below 2^31 (32-bit row offsets in a chunk)."""
+    cfg = _lib.make_config(262144, 128, 128, KDA_BF16)       # 64 * 262144 * 128 = 2^31
+    assert _fwd(cfg, T=64) == KDA_ERR_UNSUPPORTED and "H too large" in _err()
