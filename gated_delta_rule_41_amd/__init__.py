@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_FLAG_SAVE_FOR_BWD, KDA_FLAG_SEQUENTIAL, KdaConfig, KdaError, kda_bwd_workspace_size,
                    kda_fwd_workspace_size, kda_saved_size, make_config)
 
-__all__ = ["kda_fwd", "kda_bwd", "kda_decode", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
+__all__ = ["kda", "kda_fwd", "kda_bwd", "kda_decode", "kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size",
            "make_config", "KdaConfig", "KdaError", "KDA_F32", "KDA_BF16", "KDA_FLAG_SAVE_FOR_BWD",
            "KDA_FLAG_SEQUENTIAL"]
 
@@ -182,3 +182,49 @@ def kda_decode(q, k, v, g, beta, state=None, *, out_state=None, out_dtype=None, 
         _lib.check(_lib.kda_decode_raw(cfg, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                        _ptr(out_state), _ptr(o), stream))
     return o, out_state
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class KDAFunction(torch.autograd.Function):
+        """Autograd glue: forward saves the library's saved buffer, backward calls
+        kda_bwd.  Gradients flow to q, k, v, g, beta and initial_state."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, cu_seqlens, initial_state, num_seqs, eps, scale):
+            o, sf, saved = kda_fwd(q, k, v, g, beta, cu_seqlens, initial_state, num_seqs=num_seqs, eps=eps,
+                                   scale=scale, save_for_bwd=True)
+            ctx.save_for_backward(q, k, v, g, beta, saved)
+            ctx.cu_seqlens, ctx.initial_state = cu_seqlens, initial_state
+            ctx.num_seqs, ctx.eps, ctx.scale = num_seqs, eps, scale
+            ctx.out_dtype = o.dtype
+            return o, sf
+
+        @staticmethod
+        def backward(ctx, d_o, d_sf):
+            q, k, v, g, beta, saved = ctx.saved_tensors
+            s0 = ctx.initial_state
+            d_o = (d_o if d_o is not None else torch.zeros_like(v)).to(q.dtype).contiguous()
+            d_sf = d_sf.contiguous() if d_sf is not None else None
+            gr = kda_bwd(q, k, v, g, beta, saved, d_o, ctx.cu_seqlens, s0, d_sf, num_seqs=ctx.num_seqs,
+                         eps=ctx.eps, scale=ctx.scale, output_d_initial_state=s0 is not None)
+            cast = lambda t, ref: t.to(ref.dtype)  # noqa: E731
+            return (cast(gr["dq"], q), cast(gr["dk"], k), cast(gr["dv"], v), cast(gr["dg"], g),
+                    cast(gr["dbeta"], beta), None, gr["dS0"], None, None, None)
+
+    return KDAFunction
+
+
+_KDA_FN = None
+
+
+def kda(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: Optional[int] = None,
+        eps: float = 1e-6, scale: float = 1.0):
+    """KDA as a differentiable torch op: returns ``(o, final_state)`` (fp32) and,
+    under autograd, back-propagates through kda_bwd.  The upstream gradient of o
+    is cast to the input dtype (bf16 inputs take a bf16 dO, as kda_bwd does)."""
+    global _KDA_FN
+    if _KDA_FN is None:
+        _KDA_FN = _autograd_function()
+    return _KDA_FN.apply(q, k, v, g, beta, cu_seqlens, initial_state, num_seqs, eps, scale)
