@@ -33,6 +33,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct V8;
 template <> struct V8<bf16> { typedef bf16x8 t; };
@@ -83,13 +84,44 @@ template <> __device__ __forceinline__ bf16x4 pack4<bf16>(f32x4 x) { return __bu
 template <> __device__ __forceinline__ f32x4 pack4<float>(f32x4 x) { return x; }
 
 
+// The exact fp32 values of packed bf16 elements, taken from the bit pattern
+// (element 2j in the low half of dword j, element 2j+1 in the high half): one
+// shift or mask per value.  Written on the integer bits so that the compiler
+// does not rebuild each value with a scalar conversion of its own.
 __device__ __forceinline__ f32x4 unpack4(bf16x4 x) {
+    const u32x2 w = __builtin_bit_cast(u32x2, x);
     f32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = (float)x[j];
+    r[0] = __uint_as_float(w[0] << 16);
+    r[1] = __uint_as_float(w[0] & 0xffff0000u);
+    r[2] = __uint_as_float(w[1] << 16);
+    r[3] = __uint_as_float(w[1] & 0xffff0000u);
     return r;
 }
 __device__ __forceinline__ f32x4 unpack4(f32x4 x) { return x; }
+
+// hi = bf16(x), lo = bf16(x - hi) for N = 2 or 4 values held as N-element
+// bf16 vectors (the pair carries ~16 mantissa bits); hi is unpacked from its
+// bits as in unpack4.
+template <int N>
+__device__ __forceinline__ void split_n(const float (&x)[N], __bf16 __attribute__((ext_vector_type(N)))& hi,
+                                        __bf16 __attribute__((ext_vector_type(N)))& lo) {
+    static_assert(N == 2 || N == 4, "split_n: 2 or 4 values");
+    typedef float FV __attribute__((ext_vector_type(N)));
+    typedef __bf16 BV __attribute__((ext_vector_type(N)));
+    typedef unsigned WV __attribute__((ext_vector_type(N / 2)));
+    FV xv;
+#pragma unroll
+    for (int j = 0; j < N; ++j) xv[j] = x[j];
+    hi = __builtin_convertvector(xv, BV);
+    const WV w = __builtin_bit_cast(WV, hi);
+    FV h;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        h[2 * j] = __uint_as_float(w[j] << 16);
+        h[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+    lo = __builtin_convertvector(xv - h, BV);
+}
 
 // hi = T(x); lo = T(x - hi) when SPLIT (the pair carries ~16 mantissa bits).
 template <typename T, bool SPLIT>
@@ -100,13 +132,12 @@ __device__ __forceinline__ void sts4_split(T* hi, T* lo, f32x4 x) {
 }
 template <typename T, bool SPLIT>
 __device__ __forceinline__ void split8(f32x4 a, f32x4 b, typename V8<T>::t& hi, typename V8<T>::t& lo) {
-    hi = pack8<T>(a, b);
     if constexpr (SPLIT) {
-        f32x4 ra, rb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { ra[j] = a[j] - to_f32(hi[j]); rb[j] = b[j] - to_f32(hi[j + 4]); }
-        lo = pack8<T>(ra, rb);
+        const typename V4<T>::t ha = pack4<T>(a), hb = pack4<T>(b);
+        hi = __builtin_shufflevector(ha, hb, 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = pack8<T>(a - unpack4(ha), b - unpack4(hb));
     } else {
+        hi = pack8<T>(a, b);
         lo = hi;
     }
 }

@@ -643,14 +643,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 vi[e] = (rk[i][e] * ai) * gin;
             }
             VH qh, ql, kg, kih;
+            split_n<CPH>(vq, qh, ql);
+            split_n<CPH>(vi, kih, xkil[i]);
 #pragma unroll
-            for (int e = 0; e < CPH; ++e) {
-                qh[e] = from_f32<T>(vq[e]);
-                ql[e] = from_f32<T>(vq[e] - to_f32(qh[e]));
-                kg[e] = from_f32<T>(vk[e]);
-                kih[e] = from_f32<T>(vi[e]);
-                xkil[i][e] = from_f32<T>(vi[e] - to_f32(kih[e]));
-            }
+            for (int e = 0; e < CPH; ++e) kg[e] = from_f32<T>(vk[e]);
             if (!MAP) {
                 *reinterpret_cast<VH*>(&sm.qg[r * PK + pc0]) = qh;
                 *reinterpret_cast<VH*>(&sm.qgl[r * PK + pc0]) = ql;
@@ -664,8 +660,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 const int r = r0 + i;
                 if (cl == 0) sm.beta[r] = beta[i];
                 if (SAVE && slice == 0 && cl == 0 && r < Lp) {
-                    p.nq_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nq[i]);
-                    p.nk_saved[(c0 + r) * H + h] = __builtin_amdgcn_rcpf(nk[i]);
+                    const int64_t nb = c0 * H + h;   // uniform base; the row offset r*H fits in 32 bits
+                    p.nq_saved[nb + r * H] = __builtin_amdgcn_rcpf(nq[i]);
+                    p.nk_saved[nb + r * H] = __builtin_amdgcn_rcpf(nk[i]);
                 }
             }
 #pragma unroll
@@ -793,7 +790,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         for (int pass = 0; pass < 4; ++pass) {
             const int r = 16 * pass + rr;
             const f32x4 x = *reinterpret_cast<const f32x4*>(&ot[r * kOStride + 4 * cg]);
-            if (r < nrows) sts4<E>(dst + r * ld + 4 * cg, x);
+            if (r < nrows) sts4<E>(dst + (r * (int)ld + 4 * cg), x);   // r * ld < 2^31 (checked on the host)
         }
     };
 
@@ -832,7 +829,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+                    for (int i = 0; i < 4; ++i) st[(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
             }
             lds_barrier();
             // 2
@@ -900,7 +897,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ub[(int64_t)(16 * i + 4 * qg + j) * dv] = Ut[i][j];
+                    for (int j = 0; j < 4; ++j) ub[(16 * i + 4 * qg + j) * dv] = Ut[i][j];
             }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
