@@ -1034,29 +1034,27 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     auto prep_fill = [&](Prep& P, bool first, auto after_loads) {
         RawRow<T, CPH> rg[4];
         float rb[4], nq[4], nk[4];
+        // rows past the chunk end load the last row (in bounds) and are zeroed
+        // below, once every load of the chunk is in flight
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i;
-            rb[i] = 0.f; nq[i] = 1.f; nk[i] = 1.f;
-            if (r < L) {
-                P.q[i].load(qc + (r * rk32 + ck0));
-                P.k[i].load(kc + (r * rk32 + ck0));
-                rg[i].load(gcp + (r * rk32 + ck0));
-                rb[i] = gload1(bc + r * H);
-                nq[i] = nqc[r * H];     // norms saved by the forward
-                nk[i] = nkc[r * H];
-            } else {
-                P.q[i].zero(); P.k[i].zero(); rg[i].zero();
-            }
+            const int rc = min(r0 + i, L - 1);
+            P.q[i].load(qc + (rc * rk32 + ck0));
+            P.k[i].load(kc + (rc * rk32 + ck0));
+            rg[i].load(gcp + (rc * rk32 + ck0));
+            rb[i] = gload1(bc + rc * H);
+            nq[i] = nqc[rc * H];     // norms saved by the forward
+            nk[i] = nkc[rc * H];
         }
         after_loads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i;
+            const bool ok = r0 + i < L;
+            P.q[i].keep(ok); P.k[i].keep(ok); rg[i].keep(ok);
             // v_rcp (~1 ulp), as the forward forms beta and the reciprocal norms
-            P.beta[i] = (r < L) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
-            P.iq[i] = p.scale * __builtin_amdgcn_rcpf(nq[i]);
-            P.ik[i] = __builtin_amdgcn_rcpf(nk[i]);
+            P.beta[i] = ok ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
+            P.iq[i] = p.scale * __builtin_amdgcn_rcpf(ok ? nq[i] : 1.f);
+            P.ik[i] = __builtin_amdgcn_rcpf(ok ? nk[i] : 1.f);
         }
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
@@ -1144,10 +1142,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i;
-            if (r < L) { vvr[i].load(vc + (r * rv32 + cv0)); ddr[i].load(doc + (r * rv32 + cv0)); }
-            else { vvr[i].zero(); ddr[i].zero(); }
+        for (int i = 0; i < 4; ++i) {   // zeroed past the chunk end when staged
+            const int rc = min(r0 + i, L - 1);
+            vvr[i].load(vc + (rc * rv32 + cv0));
+            ddr[i].load(doc + (rc * rv32 + cv0));
         }
     });
     if (wl == 0 && qg == 0) {
@@ -1249,6 +1247,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6), v rm (slot 2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        ddr[i].keep(r0 + i < L);
+        vvr[i].keep(r0 + i < L);
         *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (r0 + i) * PV + cv0) = ddr[i].x;
         *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (r0 + i) * PV + cv0) = vvr[i].x;
     }
@@ -1262,7 +1262,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     lds_barrier();
 
     // ================= dBV = T^T dU  ->  dv, dbeta (v part) =================
-    float dbv_part[4][4];   // this wave's share of sum_j v dBV per row (waves 4-7 add theirs later)
     if (vact) {
         TO* __restrict__ dvp = reinterpret_cast<TO*>(p.dv_out) + c0 * rsv + h * DV;
         float rowpart[4][4];
@@ -1292,13 +1291,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 }
             }
         }
+        // waves 0-3 write their row sums; waves 4-7 park theirs in sred (unused
+        // until the chain rule) and add them after the next barrier
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float s = row16_sum(rowpart[mb][i]);
-                dbv_part[mb][i] = s;
-                if (w < 4 && cl == 0) sdbv[w * 64 + 16 * mb + 4 * qg + i] = s;
+                if (cl == 0) (w < 4 ? sdbv : sred)[(w & 3) * 64 + 16 * mb + 4 * qg + i] = s;
             }
     }
     // ================= dAqk = lower(dO U^T);  dT = (dU v^T) diag(beta) (waves 0-3) =================
@@ -1367,7 +1367,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sdbv[(w - 4) * 64 + 16 * mb + 4 * qg + i] += dbv_part[mb][i];
+            for (int i = 0; i < 4; ++i) {
+                const int o = (w - 4) * 64 + 16 * mb + 4 * qg + i;
+                sdbv[o] += sred[o];
+            }
     }
     {
     Prep P;

@@ -257,6 +257,10 @@ template <int N> struct RawRow<bf16, N> {
     u16n x;
     __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const u16n*>(p); }
     __device__ __forceinline__ void zero() { x = (u16n)0; }
+    // zero unless ok: applied after an unconditional load (of a clamped,
+    // in-bounds row), where the values are first needed, so that no branch
+    // around the load makes the compiler wait for its data early
+    __device__ __forceinline__ void keep(bool ok) { x = ok ? x : (u16n)0; }
     __device__ __forceinline__ float operator[](int j) const { return __uint_as_float(((unsigned)x[j]) << 16); }
     // Hide the value from the optimiser so widened copies made before this
     // point are not kept alive for uses after it.
@@ -267,6 +271,7 @@ template <int N> struct RawRow<float, N> {
     fn x;
     __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const fn*>(p); }
     __device__ __forceinline__ void zero() { x = (fn)0.f; }
+    __device__ __forceinline__ void keep(bool ok) { x = ok ? x : (fn)0.f; }
     __device__ __forceinline__ float operator[](int j) const { return x[j]; }
     __device__ __forceinline__ void fence() { asm volatile("" : "+v"(x)); }
 };
