@@ -1128,7 +1128,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     RawRow<T, VPH> ddr[4], vvr[4];   // dO and v rows of this lane (prep layout), staged in LDS later
     {
     Prep P;
-    prep_fill(P, true, [&]() {
+    prep_fill(P, true, [] {});
+    if (wl == 0 && qg == 0) {
+#pragma unroll
+        for (int e = 0; e < CPH; ++e) sgc[ck0 + e] = fast_exp2(P.GC[e]);
+    }
+    if (wh == 0 && cl == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sbeta[r0 + i] = P.beta[i];
+    }
+    put_rm(P, S(2), S(2), vKI, false);   // KI  h
+    put_rm(P, S(4), S(4), vKG, false);   // KG  h
+    lds_barrier();
+    {
         if (vact) {
             const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
             const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
@@ -1147,18 +1159,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             vvr[i].load(vc + (rc * rv32 + cv0));
             ddr[i].load(doc + (rc * rv32 + cv0));
         }
-    });
-    if (wl == 0 && qg == 0) {
-#pragma unroll
-        for (int e = 0; e < CPH; ++e) sgc[ck0 + e] = fast_exp2(P.GC[e]);
     }
-    if (wh == 0 && cl == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sbeta[r0 + i] = P.beta[i];
-    }
-    put_rm(P, S(2), S(2), vKI, false);   // KI  h
-    put_rm(P, S(4), S(4), vKG, false);   // KG  h
-    lds_barrier();
 
     // S0 / dS1 row fragments of key column block 16w for dQG, dW and dKtil,
     // issued here so that their latency hides under Akk, T and the staging
