@@ -606,8 +606,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 const int r = 16 * ib + 4 * qg + i;
                 const float vq = s <= r ? aqk[i] : 0.f;
                 const T hi = from_f32<T>(vq);
-                sm.aqt[s * PC + perm32(r)] = hi;
-                sm.aqtl[s * PC + perm32(r)] = from_f32<T>(vq - to_f32(hi));
+                sm.aqt[kt_off(s, perm32(r))] = hi;
+                sm.aqtl[kt_off(s, perm32(r))] = from_f32<T>(vq - to_f32(hi));
                 const float vk = s < r ? akk[i] : 0.f;
                 sm.akk[r * PC + s] = from_f32<T>(vk);
                 if (ib == jb) sm.adiag[ib][4 * qg + i][cl] = vk;
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sts4<T>(&sm.wt[(nb + cl) * PC + perm32(16 * i + 4 * qg)], -X[i]);
+            for (int i = 0; i < 4; ++i) sts4<T>(&sm.wt[kt_off(nb + cl, perm32(16 * i + 4 * qg))], -X[i]);
         }
     };
 
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             refresh();
             V8T dof[2], duf[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + (16 * ww + cl) * PC + 32 * kk + 8 * qg);
+            for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + kt_off(16 * ww + cl, 32 * kk + 8 * qg));
             {
                 V8T dsh[NKB], dsl[NKB];
 #pragma unroll
@@ -694,11 +694,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    const int ra = (16 * i + cl) * PC + 8 * qg;
 #pragma unroll
                     for (int kk = (i >> 1); kk < 2; ++kk) {
-                        acc = mma_k32(acc, lds8<T>(sm.aqt + ra + 32 * kk), dof[kk]);
-                        acc = mma_k32(acc, lds8<T>(sm.aqtl + ra + 32 * kk), dof[kk]);
+                        const int ra = kt_off(16 * i + cl, 32 * kk + 8 * qg);
+                        acc = mma_k32(acc, lds8<T>(sm.aqt + ra), dof[kk]);
+                        acc = mma_k32(acc, lds8<T>(sm.aqtl + ra), dof[kk]);
                     }
                     const int rk2 = (16 * i + cl) * PK + 8 * qg;
 #pragma unroll
@@ -728,7 +728,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     const int rt = kt_off(16 * mb + cl, 32 * kk + 8 * qg);
                     acc = mma_k32(acc, lds8<T>(sm.r0 + rt), dof[kk]);
                     acc = mma_k32(acc, lds8<T>(sm.r1 + rt), dof[kk]);
-                    acc = mma_k32(acc, lds8<T>(sm.wt + (16 * mb + cl) * PC + 32 * kk + 8 * qg), duf[kk]);
+                    acc = mma_k32(acc, lds8<T>(sm.wt + kt_off(16 * mb + cl, 32 * kk + 8 * qg)), duf[kk]);
                 }
                 dS[mb] = acc;
             }
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
                 for (int e = 0; e < VPL; ++e) {
                     f32x4 x = {xdo[0][e], xdo[1][e], xdo[2][e], xdo[3][e]};
-                    sts4<T>(&sm.dot[(VPL * cl + e) * PC + pr], x);   // exact: dO is an input value
+                    sts4<T>(&sm.dot[kt_off(VPL * cl + e, pr)], x);   // exact: dO is an input value
                 }
                 if (ww == 0 && qg == 0) {
 #pragma unroll

@@ -668,7 +668,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
             for (int e = 0; e < VPL; ++e) {
                 f32x4 x = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
-                sts4<T>(&sm.vt[(VPL * cl + e) * PC + r0], x);   // exact: v is an input value
+                sts4<T>(&sm.vt[kt_off(VPL * cl + e, r0)], x);   // exact: v is an input value
             }
         }
     };
@@ -731,8 +731,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 if (!MAP) {
                     const float vq = s <= r ? aqk[i] : 0.f;
                     const T hi = from_f32<T>(vq);
-                    sm.aqk[r * PC + perm32(s)] = hi;
-                    sm.aqkl[r * PC + perm32(s)] = from_f32<T>(vq - to_f32(hi));
+                    sm.aqk[kt_off(r, perm32(s))] = hi;
+                    sm.aqkl[kt_off(r, perm32(s))] = from_f32<T>(vq - to_f32(hi));
                 }
                 const float vk = s < r ? akk[i] : 0.f;
                 sm.akk[r * PC + s] = from_f32<T>(vk);
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 load_tii(tii);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f32x4 vv = lds4f<T>(&sm.vt[(16 * ww + cl) * PC + 16 * i + 4 * qg]);
+                    const f32x4 vv = lds4f<T>(&sm.vt[kt_off(16 * ww + cl, 16 * i + 4 * qg)]);
                     const f32x4 bb = *reinterpret_cast<const f32x4*>(&sm.beta[16 * i + 4 * qg]);
                     f32x4 acc = vv * bb;   // beta v, exact in fp32
 #pragma unroll
@@ -907,10 +907,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U ; next chunk's operand values
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int ra = (16 * i + cl) * PC + 8 * qg;
 #pragma unroll
                 for (int kk = 0; kk <= (i >> 1); ++kk)
-                    O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + ra + 32 * kk), lds8<T>(sm.aqkl + ra + 32 * kk), ufh[kk],
+                    O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + kt_off(16 * i + cl, 32 * kk + 8 * qg)),
+                                      lds8<T>(sm.aqkl + kt_off(16 * i + cl, 32 * kk + 8 * qg)), ufh[kk],
                                       ufl[kk]);
             }
             if (!MAP) patch_out(op + (c0 * H + h) * dv + dv0 + 16 * ww, rs_v, O, L);
