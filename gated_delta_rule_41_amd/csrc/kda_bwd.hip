@@ -455,19 +455,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                          RawRow<T, VPL> (&xd)[4], RawScalar<T> (&xb)[4], int& xl) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
         const int r0 = 16 * ww + 4 * qg;
-        const T* qc = qp + (c0 + r0) * rs_k + h * DK + CPL * cl;
-        const T* kc = kp + (c0 + r0) * rs_k + h * DK + CPL * cl;
-        const T* gc = gp + (c0 + r0) * rs_k + h * DK + CPL * cl;
-        const T* dc = dop + (c0 + r0) * rs_v + h * dv + dv0 + VPL * cl;
-        const T* bc = bp + (c0 + r0) * H + h;
+        // uniform chunk bases + 32-bit per-lane offsets (64 H max(dk, dv) < 2^31
+        // is checked on the host)
+        const T* qc = qp + (c0 * rs_k + h * DK);
+        const T* kc = kp + (c0 * rs_k + h * DK);
+        const T* gc = gp + (c0 * rs_k + h * DK);
+        const T* dc = dop + (c0 * rs_v + h * dv + dv0);
+        const T* bc = bp + (c0 * H + h);
+        const unsigned sk = (unsigned)rs_k, sv = (unsigned)rs_v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (r0 + i < L) {
-                xq[i].load(qc + i * rs_k);
-                xk[i].load(kc + i * rs_k);
-                xg[i].load(gc + i * rs_k);
-                xd[i].load(dc + i * rs_v);
-                xb[i].load(bc + i * H);
+                xq[i].load(qc + ((r0 + i) * sk + CPL * cl));
+                xk[i].load(kc + ((r0 + i) * sk + CPL * cl));
+                xg[i].load(gc + ((r0 + i) * sk + CPL * cl));
+                xd[i].load(dc + ((r0 + i) * sv + VPL * cl));
+                xb[i].load(bc + (unsigned)((r0 + i) * H));
             } else {
                 xq[i].zero(); xk[i].zero(); xg[i].zero(); xd[i].zero();
                 xb[i].zero();
@@ -656,10 +659,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             refresh();
             {
                 float* out = dst + (slot * H + h) * (int64_t)DK * dv;
+                const unsigned ob = (unsigned)(4 * qg * dv + vcol) * 4u;   // lane part of the byte offset
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) out[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
+                    for (int i = 0; i < 4; ++i) *atb(out, ob + (unsigned)((16 * mb + i) * dv) * 4u) = dS[mb][i];
             }
             lds_barrier();
             refresh();
@@ -710,11 +714,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 duf[0] = pack8<T>(dU[0], dU[1]);
                 duf[1] = pack8<T>(dU[2], dU[3]);
                 // dU of this chunk (fp32), for the chunk-parallel gradients
-                float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv + vcol;
+                float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv;
+                const unsigned ob = (unsigned)(4 * qg * dv + vcol) * 4u;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ub[(int64_t)(16 * i + 4 * qg + j) * dv] = dU[i][j];
+                    for (int j = 0; j < 4; ++j) *atb(ub, ob + (unsigned)((16 * i + j) * dv) * 4u) = dU[i][j];
             }
             lds_barrier();
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
@@ -767,10 +772,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     }
                 }
 #pragma unroll
-                for (int e = 0; e < VPL; ++e) {
-                    f32x4 x = {xdo[0][e], xdo[1][e], xdo[2][e], xdo[3][e]};
-                    sts4<T>(&sm.dot[kt_off(VPL * cl + e, pr)], x);   // exact: dO is an input value
-                }
+                for (int e = 0; e < VPL; ++e)   // dO is an input value: its bits move as they are
+                    *reinterpret_cast<V4T*>(&sm.dot[kt_off(VPL * cl + e, pr)]) =
+                        col4(xdo[0].x, xdo[1].x, xdo[2].x, xdo[3].x, e);
                 if (ww == 0 && qg == 0) {
 #pragma unroll
                     for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
@@ -787,16 +791,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 const int pr = perm32(16 * ww + 4 * qg);
 #pragma unroll
                 for (int e4 = 0; e4 < CQ; ++e4) {
-                    f32x4 hv[4], lv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) { hv[i] = unpack4(xqh[i][e4]); lv[i] = unpack4(xql[i][e4]); }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int c = CPL * cl + 4 * e4 + j;
                         *reinterpret_cast<V4T*>(&sm.r0[kt_off(c, pr)]) =
-                            pack4<T>(f32x4{hv[0][j], hv[1][j], hv[2][j], hv[3][j]});
+                            col4(xqh[0][e4], xqh[1][e4], xqh[2][e4], xqh[3][e4], j);
                         *reinterpret_cast<V4T*>(&sm.r1[kt_off(c, pr)]) =
-                            pack4<T>(f32x4{lv[0][j], lv[1][j], lv[2][j], lv[3][j]});
+                            col4(xql[0][e4], xql[1][e4], xql[2][e4], xql[3][e4], j);
                     }
                 }
             }

@@ -22,6 +22,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace kda {
 
@@ -98,6 +99,20 @@ __device__ __forceinline__ f32x4 unpack4(bf16x4 x) {
     return r;
 }
 __device__ __forceinline__ f32x4 unpack4(f32x4 x) { return x; }
+
+// Element j of four rows of four 16-bit values (bf16 bits), as one column
+// {r0[j], r1[j], r2[j], r3[j]}: two byte permutes, no conversion.
+template <typename V>
+__device__ __forceinline__ bf16x4 col4(const V& r0, const V& r1, const V& r2, const V& r3, int j) {
+    static_assert(sizeof(V) == 8, "col4: rows of four 16-bit values");
+    const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+    const u32x2 w2 = __builtin_bit_cast(u32x2, r2), w3 = __builtin_bit_cast(u32x2, r3);
+    const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;   // the high or the low half of each word
+    u32x2 out;
+    out[0] = __builtin_amdgcn_perm(w1[j >> 1], w0[j >> 1], sel);
+    out[1] = __builtin_amdgcn_perm(w3[j >> 1], w2[j >> 1], sel);
+    return __builtin_bit_cast(bf16x4, out);
+}
 
 // hi = bf16(x), lo = bf16(x - hi) for N = 2 or 4 values held as N-element
 // bf16 vectors (the pair carries ~16 mantissa bits); hi is unpacked from its
@@ -290,6 +305,18 @@ template <> struct RawScalar<float> {
     __device__ __forceinline__ void zero() { x = 0.f; }
     __device__ __forceinline__ float f() const { return x; }
 };
+
+// Element `idx` of an array whose base is uniform across the wave, addressed
+// with a 32-bit byte offset (idx * sizeof(E) < 2^32): lets the compiler use
+// the scalar-base + 32-bit vector offset form of global loads and stores
+// instead of a 64-bit address add per access.
+template <typename E>
+__device__ __forceinline__ E* atb(E* base, unsigned byte_off) {
+    typedef typename std::conditional<std::is_const<E>::value, const char, char>::type C;
+    return reinterpret_cast<E*>(reinterpret_cast<C*>(base) + byte_off);
+}
+template <typename E>
+__device__ __forceinline__ E* at32(E* base, unsigned idx) { return atb(base, idx * (unsigned)sizeof(E)); }
 
 template <typename T> __device__ __forceinline__ float gload1(const T* p) { return to_f32(*p); }
 

@@ -665,11 +665,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                     p.nk_saved[nb + r * H] = __builtin_amdgcn_rcpf(nk[i]);
                 }
             }
+            static_assert(VPL == 4, "v slice: four columns per lane");
 #pragma unroll
-            for (int e = 0; e < VPL; ++e) {
-                f32x4 x = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
-                sts4<T>(&sm.vt[kt_off(VPL * cl + e, r0)], x);   // exact: v is an input value
-            }
+            for (int e = 0; e < VPL; ++e)   // v is an input value: its bits move as they are
+                *reinterpret_cast<V4T*>(&sm.vt[kt_off(VPL * cl + e, r0)]) = col4(rv[0].x, rv[1].x, rv[2].x, rv[3].x, e);
         }
     };
     // step 1 (both groups): the tiles held in registers
@@ -829,7 +828,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) st[(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+                    for (int i = 0; i < 4; ++i) *at32(st, (16 * mb + 4 * qg + i) * dv + vcol) = S[mb][i];
             }
             lds_barrier();
             // 2
@@ -893,11 +892,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             }
             if (SAVE) {
                 // U of this chunk (fp32), for the chunk-parallel gradients
-                float* ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * dv + vcol;
+                float* ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * dv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ub[(16 * i + 4 * qg + j) * dv] = Ut[i][j];
+                    for (int j = 0; j < 4; ++j) *at32(ub, (16 * i + 4 * qg + j) * dv + vcol) = Ut[i][j];
             }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);
