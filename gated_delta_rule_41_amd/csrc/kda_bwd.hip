@@ -676,7 +676,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 f32x4 nbv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) nbv[j] = sm.adiag[ww][4 * qg + j][cl];
-                const f32x4 tw = inv_unit_lower16(na, nbv, qg, cl);
+                const f32x4 tw = inv_unit_lower16_x3(na, nbv, qg, cl);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
             }

@@ -233,6 +233,32 @@ __device__ __forceinline__ f32x4 inv_unit_lower16(f32x4 na, f32x4 nb, int qg, in
     return mma_k16(zz, -na, zz);                       // (I - N) Z
 }
 
+// The same inverse with every product taken as three bf16 MFMAs on hi/lo
+// operand pairs (hi.hi + lo.hi + hi.lo, ~16 mantissa bits): a k16 bf16 MFMA
+// pass is much shorter than the four fp32 k4 MFMAs of a k16 step, and the
+// result is rounded to bf16 before it is used as an operand anyway.
+__device__ __forceinline__ f32x4 mma3_k16(f32x4 c, f32x4 a, f32x4 b) {
+    const bf16x4 ah = pack4<bf16>(a), bh = pack4<bf16>(b);
+    const bf16x4 al = pack4<bf16>(a - unpack4(ah)), bl = pack4<bf16>(b - unpack4(bh));
+    c = mma_k16(c, ah, bh);
+    c = mma_k16(c, al, bh);
+    return mma_k16(c, ah, bl);
+}
+__device__ __forceinline__ f32x4 inv_unit_lower16_x3(f32x4 na, f32x4 nb, int qg, int cl) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = (4 * qg + i == cl) ? 1.f : 0.f;
+    const f32x4 p2 = mma3_k16(z, na, nb);
+    const f32x4 p2t = mma3_k16(z, nb, na);
+    const f32x4 p4 = mma3_k16(z, p2t, p2);
+    const f32x4 p4t = mma3_k16(z, p2, p2t);
+    const f32x4 p8 = mma3_k16(z, p4t, p4);
+    const f32x4 y = mma3_k16(eye + p4 + p8, p4t, p8);
+    const f32x4 zz = mma3_k16(y, p2t, y);
+    return mma3_k16(zz, -na, zz);
+}
+
 
 // ---------------------------------------------------- global loads/stores
 // Loads N consecutive elements of type T (N*sizeof(T) in {8,16,32} bytes)
