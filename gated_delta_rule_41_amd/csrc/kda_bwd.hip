@@ -688,6 +688,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             // 5a: dU = Aqk^T dO + Ktil dS1
             refresh();
             V8T dof[2], duf[2];
+            const KtFrag kf(qg, cl);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + kt_off(16 * ww + cl, 32 * kk + 8 * qg));
             {
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = (i >> 1); kk < 2; ++kk) {
-                        const int ra = kt_off(16 * i + cl, 32 * kk + 8 * qg);
+                        const int ra = kf.at(i, kk);
                         acc = mma_k32(acc, lds8<T>(sm.aqt + ra), dof[kk]);
                         acc = mma_k32(acc, lds8<T>(sm.aqtl + ra), dof[kk]);
                     }
@@ -724,16 +725,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             lds_barrier();
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
             refresh();
+            const KtFrag kf2(qg, cl);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
                 f32x4 acc = dS[mb] * gcv;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int rt = kt_off(16 * mb + cl, 32 * kk + 8 * qg);
+                    const int rt = kf2.at(mb, kk);
                     acc = mma_k32(acc, lds8<T>(sm.r0 + rt), dof[kk]);
                     acc = mma_k32(acc, lds8<T>(sm.r1 + rt), dof[kk]);
-                    acc = mma_k32(acc, lds8<T>(sm.wt + kt_off(16 * mb + cl, 32 * kk + 8 * qg)), duf[kk]);
+                    acc = mma_k32(acc, lds8<T>(sm.wt + kf2.at(mb, kk)), duf[kk]);
                 }
                 dS[mb] = acc;
             }

@@ -904,12 +904,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             lds_barrier();
             refresh();
             // 5b: O += Aqk U ;  S <- Diag(Gam_C) S + Ktil^T U ; next chunk's operand values
+            const KtFrag kf(qg, cl);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int kk = 0; kk <= (i >> 1); ++kk)
-                    O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + kt_off(16 * i + cl, 32 * kk + 8 * qg)),
-                                      lds8<T>(sm.aqkl + kt_off(16 * i + cl, 32 * kk + 8 * qg)), ufh[kk],
+                    O[i] = mma3<true>(O[i], lds8<T>(sm.aqk + kf.at(i, kk)), lds8<T>(sm.aqkl + kf.at(i, kk)), ufh[kk],
                                       ufl[kk]);
             }
             if (!MAP) patch_out(op + (c0 * H + h) * dv + dv0 + 16 * ww, rs_v, O, L);
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 S[mb] *= gcv;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int rt = kt_off(16 * mb + cl, 32 * kk + 8 * qg);
+                    const int rt = kf.at(mb, kk);
                     S[mb] = mma3<true>(S[mb], lds8<T>(sm.kt + rt), lds8<T>(sm.kil + rt), ufh[kk], ufl[kk]);
                 }
             }

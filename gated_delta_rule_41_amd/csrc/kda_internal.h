@@ -20,6 +20,20 @@ __device__ __forceinline__ int kt_off(int c, int pos) {
     return c * kChunk + ((((pos >> 3) ^ (c ^ (c >> 3))) & 7) << 3) + (pos & 7);
 }
 
+// kt_off of the A fragments a lane (qg, cl) reads: row 16m + cl, positions
+// 32kk + 8qg..+7, for compile-time m (0..7) and kk (0..1).  The swizzle group is
+// g0 ^ ((4kk ^ 2m) & 7) with g0 = (qg ^ cl ^ (cl >> 3)) & 7 a lane constant, so
+// four lane values and an immediate row offset cover every (m, kk).
+struct KtFrag {
+    int b[4];   // b[x] = 64 cl + ((g0 ^ 2x) << 3)
+    __device__ __forceinline__ KtFrag(int qg, int cl) {
+        const int g0 = (qg ^ cl ^ (cl >> 3)) & 7;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) b[x] = kChunk * cl + ((g0 ^ (2 * x)) << 3);
+    }
+    __device__ __forceinline__ int at(int m, int kk) const { return b[(((4 * kk) ^ (2 * m)) & 7) >> 1] + 16 * kChunk * m; }
+};
+
 // Per-chunk state slots: chunk j of sequence n uses slot floor(cu[n]/64) + n + j.
 // The map is collision-free and bounded by floor(T/64) + N (see kda_api.hip).
 inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }
