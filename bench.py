@@ -249,6 +249,22 @@ def main():
     kms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
            for j, name in enumerate(("fwd", "scan", "grads"))}
 
+    # the same step with o and the gradients written in bf16, the inputs' dtype
+    # (what the autograd wrapper returns); state, saves and accumulation stay fp32
+    out16 = kda.kda_bwd(q, k, v, g, b, saved, dO, cu_t, s0, dS, out_dtype=torch.bfloat16)
+    for _ in range(2):
+        _, _, saved16 = kda.kda_fwd(q, k, v, g, b, cu_t, s0, save_for_bwd=True, out_dtype=torch.bfloat16)
+        kda.kda_bwd(q, k, v, g, b, saved16, dO, cu_t, s0, dS, out_dtype=torch.bfloat16, out=out16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        _, _, saved16 = kda.kda_fwd(q, k, v, g, b, cu_t, s0, save_for_bwd=True, out_dtype=torch.bfloat16)
+        kda.kda_bwd(q, k, v, g, b, saved16, dO, cu_t, s0, dS, out_dtype=torch.bfloat16, out=out16)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms16 = e0.elapsed_time(e1) / args.steps
+    del out16, saved16
+
     # the inference forward on its own (no state save): the fused forward kernel alone
     n_inf = max(5, args.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -332,6 +348,8 @@ def main():
         "config": {"workload": spec["name"], "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
                    "global_batch": B, "seq_len": T, "state": "fp32", "outputs": "fp32"},
         "kernel_ms": kms,
+        "bf16_outputs": {"ms_per_step": ms16, "tokens_per_s": tokens / (ms16 * 1e-3),
+                         "note": "same step, o and gradients written in bf16"},
         "fwd_infer_ms": inf_ms,
         "fwd_infer_tokens_per_s": tokens / (inf_ms * 1e-3),
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

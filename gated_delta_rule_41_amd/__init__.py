@@ -207,11 +207,10 @@ def _autograd_function():
             s0 = ctx.initial_state
             d_o = (d_o if d_o is not None else torch.zeros_like(v)).to(q.dtype).contiguous()
             d_sf = d_sf.contiguous() if d_sf is not None else None
+            # gradients come out of the kernels in the inputs' dtype (rounded once, as a cast would)
             gr = kda_bwd(q, k, v, g, beta, saved, d_o, ctx.cu_seqlens, s0, d_sf, num_seqs=ctx.num_seqs,
-                         eps=ctx.eps, scale=ctx.scale, output_d_initial_state=s0 is not None)
-            cast = lambda t, ref: t.to(ref.dtype)  # noqa: E731
-            return (cast(gr["dq"], q), cast(gr["dk"], k), cast(gr["dv"], v), cast(gr["dg"], g),
-                    cast(gr["dbeta"], beta), None, gr["dS0"], None, None, None)
+                         out_dtype=q.dtype, eps=ctx.eps, scale=ctx.scale, output_d_initial_state=s0 is not None)
+            return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], None, gr["dS0"], None, None, None)
 
     return KDAFunction
 
