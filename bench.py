@@ -11,8 +11,12 @@ Prints ONE JSON line.  `value` is whole-job tokens/s of the fwd+bwd step with
 inputs already resident in HBM.  `roofline` reports the step's dominant kernel
 against the HBM roofline, timed with HIP events on the stream the library
 launches on; `roofline_fwd` reports the fused forward on its own (inference
-call, no state save).  `cpu_baseline` times the fp64 oracle on a bounded sample
-of the same workload on the host cores.
+call, no state save), also against the bandwidth of a plain 1 GiB device copy
+measured in the same run (`hbm_copy_gbs`) and as a fraction of the dense bf16
+MFMA peak (`mfma_frac`, useful FLOPs of the chunked form; see alg_flops_fwd).
+`bf16_outputs` times the same step with o and the gradients written in bf16.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
+on the host cores.
 
 Algorithmic bytes (inputs read once, outputs written once; what the
 implementation saves or recomputes is not counted), per kernel:
@@ -56,6 +60,17 @@ def alg_bytes(B, T, H, dk, dv, kernel):
         "grads": th * (3 * dk * 2 + dv * 2 + 2 + dv * 2) + th * (3 * dk * 4 + dv * 4 + 4),
         "scan": B * H * 2 * state,
     }[kernel]
+
+
+def alg_flops_fwd(B, T, H, dk, dv, C=64):
+    """Useful multiply-adds x 2 of the chunked forward (no recompute, triangular
+    halves counted once): per chunk and head, Akk (strict lower) and Aqk (lower)
+    over dk, the unit-lower solve for T, W = T (beta kh Gam) and Ut = T (beta v)
+    (lower), U = Ut - W S and O = (qh Gam) S (C x dk x dv each), Aqk U (lower)
+    and the state update (dk x C x dv)."""
+    lo, st = C * (C + 1) // 2, C * (C - 1) // 2
+    macs = st * dk + lo * dk + C * (C - 1) * (C - 2) // 6 + lo * dk + lo * dv + 3 * C * dk * dv + lo * dv
+    return 2.0 * macs * (B * T // C) * H
 
 
 def traffic_record(kernel):
@@ -277,6 +292,20 @@ def main():
     torch.cuda.synchronize()
     inf_ms = e0.elapsed_time(e1) / n_inf
 
+    # attainable HBM bandwidth on this GPU: one plain 1 GiB device copy (read + write)
+    cn = (1 << 30) // 4
+    csrc = torch.ones(cn, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    e0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * cn * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del csrc, cdst
+
     # the decode step on its own: one token per sequence, state updated in place
     xd = kda_inputs.generate(1005, DECODE_N, H, dk, dv, "bf16", num_seqs=DECODE_N, with_s0=True)
     dq_, dk_, dv_, dg_, db_ = (to_dev(xd[n]) for n in ("q", "k", "v", "g", "b"))
@@ -359,7 +388,11 @@ def main():
         "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd_bf16_kernel (inference, no save)",
                          "achieved": f_bytes / (inf_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes},
+                         "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes,
+                         "frac_of_copy_bw": f_bytes / (inf_ms * 1e-3) / 1e9 / copy_gbs,
+                         "mfma_frac": alg_flops_fwd(B, T, H, dk, dv) / (inf_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "alg_flop_per_launch": alg_flops_fwd(B, T, H, dk, dv)},
+        "hbm_copy_gbs": copy_gbs,
         "decode": {"workload": f"decode-bf16-N{DECODE_N}-H{H}-d{dk} (fp32 state in place)",
                    "us_per_step": dec_ms * 1e3, "tokens_per_s": DECODE_N / (dec_ms * 1e-3),
                    "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": dec_bytes / (dec_ms * 1e-3) / 1e9,
