@@ -714,13 +714,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                 }
                 duf[0] = pack8<T>(dU[0], dU[1]);
                 duf[1] = pack8<T>(dU[2], dU[3]);
-                // dU of this chunk (fp32), for the chunk-parallel gradients
+                // dU of this chunk (fp32), for the chunk-parallel gradients, stored
+                // column-major ([dv][64]) like the forward's U
                 float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv;
-                const unsigned ob = (unsigned)(4 * qg * dv + vcol) * 4u;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) *atb(ub, ob + (unsigned)((16 * i + j) * dv) * 4u) = dU[i][j];
+                    *reinterpret_cast<f32x4*>(at32(ub, vcol * kChunk + 16 * i + 4 * qg)) = dU[i];
             }
             lds_barrier();
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
@@ -1148,13 +1147,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
             const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int o = (16 * mb + 4 * qg + i) * DV + 16 * w + cl;
-                    U[mb][i] = ub[o];
-                    dU[mb][i] = dub[o];
-                }
+            for (int mb = 0; mb < 4; ++mb) {   // column-major [dv][64]: four rows per 16-byte load
+                const int o = (16 * w + cl) * kChunk + 16 * mb + 4 * qg;
+                U[mb] = *reinterpret_cast<const f32x4*>(ub + o);
+                dU[mb] = *reinterpret_cast<const f32x4*>(dub + o);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {   // zeroed past the chunk end when staged

@@ -891,12 +891,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 }
             }
             if (SAVE) {
-                // U of this chunk (fp32), for the chunk-parallel gradients
+                // U of this chunk (fp32), for the chunk-parallel gradients, stored
+                // column-major ([dv][64]): a lane's four rows are 16 contiguous bytes
                 float* ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * dv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) *at32(ub, (16 * i + 4 * qg + j) * dv + vcol) = Ut[i][j];
+                    *reinterpret_cast<f32x4*>(at32(ub, vcol * kChunk + 16 * i + 4 * qg)) = Ut[i];
             }
             split8<T, true>(Ut[0], Ut[1], ufh[0], ufl[0]);
             split8<T, true>(Ut[2], Ut[3], ufh[1], ufl[1]);

@@ -51,7 +51,7 @@ struct FwdParams {
     void* st_saved;      // [slots,H,dk,dv] state dtype, or nullptr
     float* nq_saved;     // [T,H] or nullptr
     float* nk_saved;     // [T,H] or nullptr
-    float* u_saved;      // [slots,H,64,dv] fp32: U of every chunk (bf16 inputs), or nullptr
+    float* u_saved;      // [slots,H,dv,64] fp32 (column-major per chunk): U of every chunk (bf16 inputs), or nullptr
     const int32_t* sf_dst;   // per sequence: row of sfinal to write, or -1 to skip; nullptr = itself
     int64_t T;
     int32_t N, H, dv, seqlen;
@@ -90,8 +90,8 @@ struct BwdParams {
     const void* dO;          // [T,H,dv] in dtype
     const float* dS_final;   // [N,H,dk,dv] or nullptr
     void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
-    const float* u_saved;    // forward's U of every chunk [slots,H,64,dv] (bf16 inputs)
-    float* du_ws;            // workspace: dU of every chunk [slots,H,64,dv] (bf16 inputs)
+    const float* u_saved;    // forward's U of every chunk [slots,H,dv,64] (bf16 inputs)
+    float* du_ws;            // workspace: dU of every chunk [slots,H,dv,64] (bf16 inputs)
     void* dq;
     void* dk;
     void* dv_out;
