@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const T* __restrict__ bc = reinterpret_cast<const T*>(p.b) + c0 * H + h;
     const float* __restrict__ S0 = reinterpret_cast<const float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
     const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
-    float xs0[NKV][8], xd0[NKV][8];   // S0 / dS1 row fragments (loaded before Akk)
+    float xs0[NKV][8], xd0[NKV][8];   // S0 / dS1 row fragments (loaded during Akk and T)
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const int r0 = 16 * wl + 4 * qg;             // prep layout: rows r0..r0+3
@@ -1161,15 +1161,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         }
     }
 
-    // S0 / dS1 row fragments of key column block 16w for dQG, dW and dKtil,
-    // issued here so that their latency hides under Akk, T and the staging
+    // S0 row fragments of key column block 16w for dQG and dW.  The loads of
+    // this kernel are spread over the steps before their first use (U, dU, v,
+    // dO and S0 here, dS1 two steps later): a wave stalls at issue while its
+    // memory queue is full, so issuing everything at once left Akk and T
+    // waiting behind it (measured 4% slower overall).
     if (kact) {
         const int nr = 16 * w + cl;
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) {
-            gf8(xs0[kk], S0 + (nr * DV + 32 * kk + 8 * qg));
-            gf8(xd0[kk], dS1 + (nr * DV + 32 * kk + 8 * qg));
-        }
+        for (int kk = 0; kk < NKV; ++kk) gf8(xs0[kk], S0 + (nr * DV + 32 * kk + 8 * qg));
     }
     // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
@@ -1207,6 +1207,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         for (int i = 0; i < 4; ++i) Tf[(16 * w + 4 * qg + i) * PF + 16 * w + cl] = tw[i];
     }
     lds_barrier();
+    // dS1 row fragments of key column block 16w, for dKtil
+    if (kact) {
+        const int nr = 16 * w + cl;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) gf8(xd0[kk], dS1 + (nr * DV + 32 * kk + 8 * qg));
+    }
     // off-diagonal blocks, column j on wave j: T_ij = -T_ii sum_{k=j}^{i-1} Akk_ik T_kj
     {
         auto solve_col = [&](auto jcst) {
