@@ -820,23 +820,32 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk, ++slot) {
             const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
             const bool more = c0 + kChunk < t1;
+            // The entering state of this chunk (fp32) is saved a quarter per step
+            // over steps 1-4 (S changes only in 5b): a wave stalls at issue while
+            // its memory queue is full, so the stores go out beside the work.
+            auto save_state = [&](int part) {
+                if (SAVE) {
+                    float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
+                    constexpr int PER = NMB / 4;
+#pragma unroll
+                    for (int mb = part * PER; mb < (part + 1) * PER; ++mb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) *at32(st, (16 * mb + 4 * qg + i) * dv + vcol) = S[mb][i];
+                }
+            };
             refresh();
-            // 1: held tiles; save the entering state of this chunk (fp32)
+            // 1: held tiles
             store_held();
-            if (SAVE) {
-                float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) *at32(st, (16 * mb + 4 * qg + i) * dv + vcol) = S[mb][i];
-            }
+            save_state(0);
             lds_barrier();
             // 2
             refresh();
+            save_state(1);
             intra_products();
             lds_barrier();
             // 3: (I + Akk_bb)^{-1}, block b = this wave; Ktil^T of this half
             refresh();
+            save_state(2);
             {
                 const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
                 f32x4 nb;
@@ -851,6 +860,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             // 4: Ut = (I + Akk)^{-1} diag(beta) v for this wave's 16 value columns
             //    (and, at dk = 128, W for key column block ww + 4)
             refresh();
+            save_state(3);
             f32x4 Ut[4];
             {
                 V4T tii[4];
