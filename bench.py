@@ -101,7 +101,7 @@ def decode_bytes(N, H, dk, dv):
 FWD_GRID = 4 * 32 * 2 * 512   # threads in one launch of the workload's fused forward (one per chain and slice)
 
 KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file, grid size or None)
-    "grads": ("kda_bwd_grads_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
+    "grads": ("kda_bwd_grads_kernel<float, 128, 128>", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
     "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
     "fwd": ("kda_fwd_bf16_kernel<float, 128, true, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip", FWD_GRID),
     # the long-context run's second level launches the same kernel on another grid
