@@ -540,7 +540,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     VH xkil[4];                             // kh/Gam lo of the next chunk to run
     float xgc[CPH];                         // Gam_C of the next chunk to run
 
-    auto load_chunk = [&](int64_t c0) {
+    // The rows of a chunk load in three parts (0: q and beta, 1: k, 2: g and the
+    // v slice), issued in different steps: a wave stalls at issue while its
+    // memory queue is full, so one burst of every load left the end of the
+    // chunk waiting behind it.  load_chunk issues all three.
+    auto load_part = [&](int64_t c0, int part) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
         // uniform chunk bases (scalar registers) + 32-bit per-lane offsets
         const T* qc = qp + c0 * rs_k + h * DK;
@@ -553,22 +557,28 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (r0 + i < L) {
-                if (MAP) rq[i].zero();   // the maps need no queries
-                else rq[i].load(qc + (ok + i * sk));
-                rk[i].load(kc + (ok + i * sk));
-                rg[i].load(gc + (ok + i * sk));
-                if (!is_state) {
-                    if (mslice) rv[i].zero();
-                    else rv[i].load(vc + (ov + i * sv));
+                if (part == 0) {
+                    if (MAP) rq[i].zero();   // the maps need no queries
+                    else rq[i].load(qc + (ok + i * sk));
+                    rb[i].load(bc + (ob + i * H));
+                } else if (part == 1) {
+                    rk[i].load(kc + (ok + i * sk));
+                } else {
+                    rg[i].load(gc + (ok + i * sk));
+                    if (!is_state) {
+                        if (mslice) rv[i].zero();
+                        else rv[i].load(vc + (ov + i * sv));
+                    }
                 }
-                rb[i].load(bc + (ob + i * H));
             } else {
-                rq[i].zero(); rk[i].zero(); rg[i].zero(); rv[i].zero();
-                rb[i].zero();
+                if (part == 0) { rq[i].zero(); rb[i].zero(); }
+                else if (part == 1) rk[i].zero();
+                else { rg[i].zero(); rv[i].zero(); }
             }
         }
-        Lp = L;
+        if (part == 0) Lp = L;
     };
+    auto load_chunk = [&](int64_t c0) { load_part(c0, 0); load_part(c0, 1); load_part(c0, 2); };
     // In-wave inclusive prefix of the gates over the wave's 16 rows, for key
     // column ck0+e: one k16 MFMA of the lower-triangular ones matrix with the raw
     // bf16 gates, which already sit in B-fragment layout (lane (qg, cl) holds
@@ -800,7 +810,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         prep_a();
         lds_barrier();
         prep_b(t0);
-        if (t0 + kChunk < t1) load_chunk(t0 + kChunk);
+        if (t0 + kChunk < t1) load_part(t0 + kChunk, 0);   // parts 1 and 2 in steps 1 and 2
     }
     if (is_state) {
         // ---------------------------------------------------------------- state waves
@@ -835,11 +845,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             };
             refresh();
             // 1: held tiles
+            if (more) load_part(c0 + kChunk, 1);
             store_held();
             save_state(0);
             lds_barrier();
             // 2
             refresh();
+            if (more) load_part(c0 + kChunk, 2);
             save_state(1);
             intra_products();
             lds_barrier();
@@ -935,7 +947,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             }
             if (more) {
                 prep_b(c0 + kChunk);
-                if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);
+                if (c0 + 2 * kChunk < t1) load_part(c0 + 2 * kChunk, 0);
             }
             lds_barrier();
         }
@@ -952,9 +964,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         for (int64_t c0 = t0; c0 < t1; c0 += kChunk) {
             const bool more = c0 + kChunk < t1;
             refresh();
+            if (more) load_part(c0 + kChunk, 1);
             store_held();
             lds_barrier();
             refresh();
+            if (more) load_part(c0 + kChunk, 2);
             intra_products();
             lds_barrier();
             refresh();
@@ -974,7 +988,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
             refresh();
             if (more) {
                 prep_b(c0 + kChunk);
-                if (c0 + 2 * kChunk < t1) load_chunk(c0 + 2 * kChunk);
+                if (c0 + 2 * kChunk < t1) load_part(c0 + 2 * kChunk, 0);
             }
             lds_barrier();
         }
