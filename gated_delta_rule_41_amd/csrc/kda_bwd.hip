@@ -451,8 +451,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     RawRow<T, VPL> xdo[4];        // its dO slice
     float xgc[CPL];               // its Gam_C
 
+    // part: -1 all rows; 0 q and beta; 1 k; 2 g and dO.  The second buffer is
+    // filled in parts over three steps: a wave stalls at issue while its
+    // memory queue is full, and one burst held up the step that issued it.
     auto load_rows = [&](int64_t c0, RawRow<T, CPL> (&xq)[4], RawRow<T, CPL> (&xk)[4], RawRow<T, CPL> (&xg)[4],
-                         RawRow<T, VPL> (&xd)[4], RawScalar<T> (&xb)[4], int& xl) {
+                         RawRow<T, VPL> (&xd)[4], RawScalar<T> (&xb)[4], int& xl, int part) {
         const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
         const int r0 = 16 * ww + 4 * qg;
         // uniform chunk bases + 32-bit per-lane offsets (64 H max(dk, dv) < 2^31
@@ -466,20 +469,25 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (r0 + i < L) {
-                xq[i].load(qc + ((r0 + i) * sk + CPL * cl));
-                xk[i].load(kc + ((r0 + i) * sk + CPL * cl));
-                xg[i].load(gc + ((r0 + i) * sk + CPL * cl));
-                xd[i].load(dc + ((r0 + i) * sv + VPL * cl));
-                xb[i].load(bc + (unsigned)((r0 + i) * H));
+                if (part <= 0) {
+                    xq[i].load(qc + ((r0 + i) * sk + CPL * cl));
+                    xb[i].load(bc + (unsigned)((r0 + i) * H));
+                }
+                if (part < 0 || part == 1) xk[i].load(kc + ((r0 + i) * sk + CPL * cl));
+                if (part < 0 || part == 2) {
+                    xg[i].load(gc + ((r0 + i) * sk + CPL * cl));
+                    xd[i].load(dc + ((r0 + i) * sv + VPL * cl));
+                }
             } else {
-                xq[i].zero(); xk[i].zero(); xg[i].zero(); xd[i].zero();
-                xb[i].zero();
+                if (part <= 0) { xq[i].zero(); xb[i].zero(); }
+                if (part < 0 || part == 1) xk[i].zero();
+                if (part < 0 || part == 2) { xg[i].zero(); xd[i].zero(); }
             }
         }
-        xl = L;
+        if (part <= 0) xl = L;
     };
-    auto load_chunk = [&](int64_t c0) { load_rows(c0, rq, rk, rg, rdo, rb, Lp); };
-    auto load_next = [&](int64_t c0) { load_rows(c0, nrq, nrk, nrg, nrdo, nrb, nLp); };
+    auto load_chunk = [&](int64_t c0) { load_rows(c0, rq, rk, rg, rdo, rb, Lp, -1); };
+    auto load_next = [&](int64_t c0, int part) { load_rows(c0, nrq, nrk, nrg, nrdo, nrb, nLp, part); };
     auto take_next = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -783,11 +791,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             }
             lds_barrier();
             refresh();
-            if (jc > 1) load_next(c0 - 2 * kChunk);   // rows of the chunk before the previous one
+            if (jc > 1) load_next(c0 - 2 * kChunk, 0);   // rows of the chunk before the previous one
             intra_products();
             lds_barrier();
             // 3: (qh Gam)^T hi/lo over the qh Gam tiles (swizzled layout); half of Ktil
             refresh();
+            if (jc > 1) load_next(c0 - 2 * kChunk, 1);
             {
                 const int pr = perm32(16 * ww + 4 * qg);
 #pragma unroll
@@ -805,6 +814,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             ktil_in_place(2);
             lds_barrier();
             refresh();
+            if (jc > 1) load_next(c0 - 2 * kChunk, 2);
             w_solve();
             lds_barrier();
             // 5a: norms, sigmoid and gate sums of the previous chunk
