@@ -900,15 +900,25 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
                 V8T sfh[NKB], sfl[NKB];
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk) split8<T, true>(S[2 * kk], S[2 * kk + 1], sfh[kk], sfl[kk]);
+                // k-step outer: the twelve fragments of a step are read together
+                // and feed four independent accumulator chains, so the LDS
+                // latency is paid once per step rather than before every MFMA
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ro = (16 * i + cl) * PK + 8 * qg;
-                    O[i] = zero;
+                for (int i = 0; i < 4; ++i) O[i] = zero;
 #pragma unroll
-                    for (int kk = 0; kk < NKB; ++kk) {
-                        Ut[i] = mma_k32(Ut[i], lds8<T>(sm.ki + ro + 32 * kk), sfh[kk]);
-                        O[i] = mma3<true>(O[i], lds8<T>(sm.qg + ro + 32 * kk), lds8<T>(sm.qgl + ro + 32 * kk), sfh[kk],
-                                          sfl[kk]);
+                for (int kk = 0; kk < NKB; ++kk) {
+                    V8T aw[4], ah[4], al[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ro = (16 * i + cl) * PK + 8 * qg + 32 * kk;
+                        aw[i] = lds8<T>(sm.ki + ro);
+                        ah[i] = lds8<T>(sm.qg + ro);
+                        al[i] = lds8<T>(sm.qgl + ro);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        Ut[i] = mma_k32(Ut[i], aw[i], sfh[kk]);
+                        O[i] = mma3<true>(O[i], ah[i], al[i], sfh[kk], sfl[kk]);
                     }
                 }
             }
