@@ -164,6 +164,47 @@ def pmc_summary(fetch_csv, write_csv, probe_mib):
           f"{p['WRITE_SIZE']['kib']:.0f} KiB (scale {p['WRITE_SIZE']['scale']:.4f})")
 
 
+def counter_summary(paths):
+    """Per-dispatch averages of every SQ counter in rocprofv3 --pmc CSV files
+    for the bench kernels (no GPU work), with the derived busy fractions:
+      waves issuing   SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES
+      VALU issuing    SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES   (per wave; a SIMD
+                      runs two waves of these kernels)
+      MFMA busy       SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES)
+                      (reading the first as summed over the four SIMDs of a CU)
+      LDS conflicts   SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE"""
+    import csv
+    vals = {}
+    for path in paths:
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name, gs, counter), v in per.items():
+            for k, (needle, _, grid) in KERNELS.items():
+                if needle in name and (grid is None or gs == grid):
+                    vals.setdefault(k, {}).setdefault(counter, []).append(v)
+    out = {}
+    for k, cs in vals.items():
+        a = {c: sum(v) / len(v) for c, v in cs.items()}
+
+        def ratio(num, den, mul=1.0):
+            return a[num] / (mul * a[den]) if num in a and den in a and a[den] else None
+        out[k] = {"counters": a,
+                  "waves_issuing": ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+                  "valu_issuing_per_wave": ratio("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+                  "mfma_busy": ratio("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", 4.0),
+                  "lds_conflict_share": ratio("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")}
+    print("| kernel | waves issuing | VALU issuing (per wave) | MFMA busy | LDS cycles in bank conflicts |")
+    print("|---|---|---|---|---|")
+    fmt = lambda x: "-" if x is None else f"{100 * x:.1f}%"   # noqa: E731
+    for k, r in out.items():
+        print(f"| {KERNELS[k][0]} | {fmt(r['waves_issuing'])} | {fmt(r['valu_issuing_per_wave'])} | "
+              f"{fmt(r['mfma_busy'])} | {fmt(r['lds_conflict_share'])} |")
+    return out
+
+
 def cpu_baseline(x, cu, spec, heads):
     """fp64 oracle, forward + backward, on the first sequence and `heads` heads."""
     import numpy as np
@@ -195,10 +236,16 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed run, one plain device copy of this many MiB (the reference "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="no GPU work: per-kernel averages and busy fractions of the SQ counters in "
+                         "rocprofv3 --pmc counter files of a bench run")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE counter files of "
                          "a run with --copy-probe-mib into profiles/traffic.json and print a summary")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.pmc_summary:
         if args.copy_probe_mib <= 0:
             ap.error("--pmc-summary needs the --copy-probe-mib value of the profiled run")
