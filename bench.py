@@ -205,25 +205,29 @@ def counter_summary(paths):
     return out
 
 
-def cpu_baseline(x, cu, spec, heads):
-    """fp64 oracle, forward + backward, on the first sequence and `heads` heads."""
+def cpu_baseline(x, cu, spec, seqs, heads):
+    """fp64 oracle, forward + backward, on the first `seqs` sequences and the
+    first `heads` heads of the workload (one oracle thread per (sequence, head)
+    chain, at most the cores this process may use)."""
     import numpy as np
 
     import oracle
 
     T = spec["T"]
-    sel = {k: np.ascontiguousarray(x[k][:T, :heads]) for k in ("q", "k", "v", "g", "b", "dO")}
-    s0 = np.ascontiguousarray(x["s0"][:1, :heads])
-    dS = np.ascontiguousarray(x["dS"][:1, :heads])
-    threads = min(oracle.default_threads(), heads)
+    n = seqs * T
+    sel = {k: np.ascontiguousarray(x[k][:n, :heads]) for k in ("q", "k", "v", "g", "b", "dO")}
+    s0 = np.ascontiguousarray(x["s0"][:seqs, :heads])
+    dS = np.ascontiguousarray(x["dS"][:seqs, :heads])
+    cu_s = np.asarray(cu[:seqs + 1], dtype=np.int64)
+    threads = min(oracle.default_threads(), seqs * heads)
     t0 = time.perf_counter()
-    oracle.fwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], initial_state=s0, threads=threads)
-    oracle.bwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], sel["dO"], initial_state=s0, dS_final=dS,
-               threads=threads)
+    oracle.fwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], cu_seqlens=cu_s, initial_state=s0, threads=threads)
+    oracle.bwd(sel["q"], sel["k"], sel["v"], sel["g"], sel["b"], sel["dO"], cu_seqlens=cu_s, initial_state=s0,
+               dS_final=dS, threads=threads)
     dt = time.perf_counter() - t0
-    full_tokens = T * heads / spec["H"]   # token-heads processed, as whole tokens of the workload
+    full_tokens = n * heads / spec["H"]   # token-heads processed, as whole tokens of the workload
     return {"value": full_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fwd+bwd of sequence 0, heads 0..{heads - 1}, T={T} ({T * heads} token-heads), "
+            "sample": f"fwd+bwd of sequences 0..{seqs - 1}, heads 0..{heads - 1}, T={T} ({n * heads} token-heads), "
                       f"{dt:.1f} s wall"}
 
 
@@ -232,7 +236,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's CPU sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's CPU sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's CPU sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed run, one plain device copy of this many MiB (the reference "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -464,7 +469,8 @@ def main():
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = 2 * n * 4
     if args.cpu_heads > 0:
-        line["cpu_baseline"] = cpu_baseline(x, cu, spec, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(x, cu, spec, max(1, min(args.cpu_seqs, spec["B"])),
+                                            min(args.cpu_heads, spec["H"]))
     print(json.dumps(line), flush=True)
 
 
