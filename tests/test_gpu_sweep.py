@@ -110,3 +110,33 @@ def test_sweep_two_level_forward(seed):
     e1, e2 = max_over_rms(host(o), o_ref), frob_rel(host(sf), sf_ref)
     _say(f"  o max/rms {e1:.2e} S_T frob {e2:.2e}")
     assert e1 <= BF16_MAX_RMS and e2 <= BF16_FROB
+
+
+@pytest.mark.parametrize("H,lens", [(24, [300, 65]), (40, [129, 1, 200])])
+def test_sweep_many_heads(H, lens):
+    """Head counts well above the other cases (token strides of H x d), short
+    ragged documents, forward and backward against the oracle."""
+    need_gpu()
+    dk = dv = 128
+    _say(f"many heads: H={H} lens={lens}")
+    cu = kda_inputs.cu_from_lengths(lens)
+    T = int(cu[-1])
+    x = kda_inputs.generate(650 + H, T, H, dk, dv, "bf16", num_seqs=len(lens), with_s0=True, with_grads=True)
+    d = {k: dev(x[k], "bf16") for k in ("q", "k", "v", "g", "b", "dO")}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    dS = torch.from_numpy(x["dS"]).cuda()
+    o, sf, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, save_for_bwd=True)
+    gr = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS)
+    torch.cuda.synchronize()
+    o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"])
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["b"], x["dO"], cu_seqlens=cu, initial_state=x["s0"],
+                     dS_final=x["dS"])
+    errs = {"o": max_over_rms(host(o), o_ref), "S_T": frob_rel(host(sf), sf_ref)}
+    for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "db")):
+        errs[name] = max_over_rms(host(gr[name]), ref[rname])
+    errs["dS0"] = frob_rel(host(gr["dS0"]), ref["dS0"])
+    _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert np.isfinite(v), k
+        assert v <= (BF16_FROB if k in ("S_T", "dS0") else BF16_MAX_RMS), (k, v)
