@@ -1,0 +1,99 @@
+"""GPU parity at the degenerate ends of the method's inputs, forward and
+backward, against the fp64 oracle through the C ABI.
+
+One call carries four heads, each at one extreme:
+  head 0  g = 0: no decay (alpha = 1, the ungated delta rule)
+  head 1  g = -1.1875 on every channel: the cumulative log-decay of a full
+          64-token chunk is -76, close to the supported floor of -80
+  head 2  beta logits of +-30: beta is 1 or 0 to within 1e-13 (full overwrite
+          or no write)
+  head 3  q and k rows that are exactly zero on every fifth token: the L2 norm
+          runs on eps alone (q^ = k^ = 0 there, and d q = d q^ / sqrt(eps))
+Errors are measured per head, so the large gradients of head 3's zero rows do
+not loosen the bar for the other heads.  Bars as in the other parity tests.
+"""
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+
+from gpu_util import dev, frob_rel, host, inf_rel, max_over_rms, need_gpu, torch
+
+import gated_delta_rule_41_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+LENS = [130, 64, 1, 77]
+
+
+def _say(msg):
+    print(f"[gpu-edge] {msg}", flush=True)
+
+
+def _inputs(dtype, dk, dv):
+    cu = kda_inputs.cu_from_lengths(LENS)
+    T = int(cu[-1])
+    x = kda_inputs.generate(95, T, 4, dk, dv, dtype, num_seqs=len(LENS), with_s0=True, with_grads=True)
+    x["g"][:, 0] = 0.0
+    x["g"][:, 1] = -1.1875                      # exact in bf16
+    x["b"][:, 2] = np.where(np.arange(T) % 2 == 0, 30.0, -30.0)
+    zero = np.arange(T) % 5 == 3
+    x["q"][zero, 3] = 0.0
+    x["k"][zero, 3] = 0.0
+    return cu, x
+
+
+def _err(a, r, dtype, state=False):
+    if dtype == "f32":
+        return inf_rel(a, r)
+    return frob_rel(a, r) if state else max_over_rms(a, r)
+
+
+def _scale(r, dtype):
+    return float(np.abs(r).max()) if dtype == "f32" else float(np.sqrt(np.mean(r * r)))
+
+
+def _bar(dtype, state=False):
+    return 1e-4 if dtype == "f32" else (1e-2 if state else 2e-2)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("bf16", 64, 128)])
+def test_degenerate_heads_forward_backward(dtype, dk, dv):
+    need_gpu()
+    _say(f"degenerate heads {dtype} dk={dk} dv={dv} lens={LENS}")
+    cu, x = _inputs(dtype, dk, dv)
+    d = {k: dev(x[k], dtype) for k in ("q", "k", "v", "g", "b", "dO")}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    dS = torch.from_numpy(x["dS"]).cuda()
+    cu_t = torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda()
+    o, sf, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, save_for_bwd=True)
+    gr = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS)
+    torch.cuda.synchronize()
+
+    o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"])
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["b"], x["dO"], cu_seqlens=cu, initial_state=x["s0"],
+                     dS_final=x["dS"])
+    got = {"o": host(o), "sf": host(sf), "dq": host(gr["dq"]), "dk": host(gr["dk"]), "dv": host(gr["dv"]),
+           "dg": host(gr["dg"]), "db": host(gr["dbeta"]), "dS0": host(gr["dS0"])}
+    want = {"o": o_ref, "sf": sf_ref, "dq": ref["dq"], "dk": ref["dk"], "dv": ref["dv"], "dg": ref["dg"],
+            "db": ref["db"], "dS0": ref["dS0"]}
+    states = ("sf", "dS0")
+    for name, a in got.items():
+        assert np.isfinite(a).all(), (dtype, name)
+    # beta'(+-30) is ~1e-13, so head 2's dbeta is measured against the scale of the other
+    # heads' dbeta (fp32 rounds sigmoid(30) to 1, so the kernel's beta (1 - beta) is 0 there:
+    # an absolute error of ~1e-13, not a relative one)
+    db_scale = want["db"][:, [0, 1, 3]]
+    for h in range(4):
+        errs = {}
+        for name, a in got.items():
+            ah, rh = a[:, h], want[name][:, h]
+            if name == "db" and h == 2:
+                errs[name] = _err(ah, rh, dtype) * (_scale(rh, dtype) / _scale(db_scale, dtype))
+            else:
+                errs[name] = _err(ah, rh, dtype, state=name in states)
+        _say(f"head {h}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for name, e in errs.items():
+            assert e <= _bar(dtype, state=name in states), (dtype, h, name, e)
+    assert np.abs(got["db"][:, 2]).max() <= 1e-9 * _scale(db_scale, "bf16")
