@@ -49,7 +49,8 @@
  *    undefined behaviour; the kernels clamp every document to
  *    [0, total_tokens) so it cannot address memory outside the buffers.
  *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
- *    {KDA_F32, KDA_BF16}; H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
+ *    {KDA_F32, KDA_BF16}, with fp32 inputs only at dk = 64 in kda_fwd and
+ *    kda_bwd (KDA_ERR_UNSUPPORTED otherwise; kda_decode takes both dk); H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
  *    kernels address a chunk's rows with 32-bit offsets; KDA_ERR_UNSUPPORTED
  *    otherwise); total_tokens < 2^31; per-chunk cumulative
  *    log-decay sum_{chunk} g >= -80 per channel (the kernels factor
