@@ -6,6 +6,7 @@ scaling the normalised query by 1/2 is exact in floating point and o is linear
 in it, so o(scale=1/2) = o(scale=1) / 2 bitwise, for the chunked forward and
 for the decode step; and the loss <dO, o> with scale s is the loss with scale 1
 and upstream gradient s dO, so the gradients agree (up to rounding).
+A non-default eps of the L2 norm is checked against the oracle at that eps.
 bf16 outputs are compared with the fp32 outputs of the same call: beyond the
 storage rounding (round to nearest, at most 2^-8 |x|) they must agree to
 1e-5 of the RMS, i.e. the bf16-output kernels compute the same values.
@@ -14,8 +15,9 @@ import numpy as np
 import pytest
 
 import kda_inputs
+import oracle
 
-from gpu_util import dev, host, max_over_rms, need_gpu, torch
+from gpu_util import dev, frob_rel, host, inf_rel, max_over_rms, need_gpu, torch
 
 import gated_delta_rule_41_amd as kda
 
@@ -116,3 +118,57 @@ def test_split_forward_bf16_output():
     _say(f"  o excess over bf16 storage {e:.2e}")
     assert e <= SAME
     assert torch.equal(sfb, sff)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_norm_eps_forward_backward_decode(dtype, dk, dv):
+    """A non-default eps of the L2 norm reaches the forward, the backward (through the saved
+    norms) and the decode step.  q and k are scaled by 1/16 (exact) so |q|^2 is ~dk/256 and
+    eps = 0.25 changes every normalised row; the runs are compared with the oracle at the
+    same eps, and the default eps is checked to give a different o (the test is not vacuous)."""
+    need_gpu()
+    eps = 0.25
+    _say(f"norm eps {eps} {dtype} dk={dk} dv={dv}")
+    lens = [150, 64, 1]
+    cu = kda_inputs.cu_from_lengths(lens)
+    T = int(cu[-1])
+    x = kda_inputs.generate(97, T, 2, dk, dv, dtype, num_seqs=len(lens), with_s0=True, with_grads=True)
+    x["q"] = x["q"] / 16.0
+    x["k"] = x["k"] / 16.0
+    d = {k: dev(x[k], dtype) for k in ("q", "k", "v", "g", "b", "dO")}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    dS = torch.from_numpy(x["dS"]).cuda()
+    o, sf, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, eps=eps, save_for_bwd=True)
+    gr = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS, eps=eps)
+    o_def, _, _ = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0)
+    # decode: the first token of every document as a one-token step from its initial state
+    first = cu[:-1][np.asarray(lens) > 0]
+    pick = lambda a: a[first]
+    dd = {k: dev(pick(x[k]), dtype) for k in ("q", "k", "v", "g", "b")}
+    s0d = torch.from_numpy(x["s0"][np.asarray(lens) > 0]).cuda()
+    o_dec, st_dec = kda.kda_decode(dd["q"], dd["k"], dd["v"], dd["g"], dd["b"], s0d, eps=eps)
+    torch.cuda.synchronize()
+
+    o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"],
+                               eps=eps)
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["b"], x["dO"], cu_seqlens=cu, initial_state=x["s0"],
+                     dS_final=x["dS"], eps=eps)
+    n1 = len(first)
+    od_ref, sd_ref = oracle.fwd(pick(x["q"]), pick(x["k"]), pick(x["v"]), pick(x["g"]), pick(x["b"]),
+                                cu_seqlens=np.arange(n1 + 1), initial_state=x["s0"][np.asarray(lens) > 0], eps=eps)
+    pairs = [("o", host(o), o_ref, False), ("sf", host(sf), sf_ref, True), ("dq", host(gr["dq"]), ref["dq"], False),
+             ("dk", host(gr["dk"]), ref["dk"], False), ("dv", host(gr["dv"]), ref["dv"], False),
+             ("dg", host(gr["dg"]), ref["dg"], False), ("db", host(gr["dbeta"]), ref["db"], False),
+             ("dS0", host(gr["dS0"]), ref["dS0"], True), ("o_dec", host(o_dec), od_ref, False),
+             ("state_dec", host(st_dec), sd_ref, True)]
+    errs = {}
+    for name, a, r, state in pairs:
+        assert np.isfinite(a).all(), name
+        errs[name] = inf_rel(a, r) if dtype == "f32" else (frob_rel(a, r) if state else max_over_rms(a, r))
+    _say(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for name, a, r, state in pairs:
+        bar = 1e-4 if dtype == "f32" else (1e-2 if state else 2e-2)
+        assert errs[name] <= bar, (name, errs[name])
+    # the default eps gives a visibly different output on these rows
+    assert max_over_rms(host(o_def), o_ref) > 0.1
