@@ -40,7 +40,8 @@ def _case(seed):
     if sum(lens) == 0:
         lens[0] = 70
     with_s0 = bool(rng.random() < 0.7)
-    return dtype, dk, dv, H, lens, with_s0
+    with_dS = bool(rng.random() < 0.7)   # drawn last: the earlier draws of every seed are unchanged
+    return dtype, dk, dv, H, lens, with_s0, with_dS
 
 
 def _bar(dtype):
@@ -56,22 +57,22 @@ def _err(dtype, a, r, state=False):
 @pytest.mark.parametrize("seed", range(12))
 def test_sweep_forward_backward(seed):
     need_gpu()
-    dtype, dk, dv, H, lens, with_s0 = _case(seed)
-    _say(f"seed {seed}: {dtype} dk={dk} dv={dv} H={H} lens={lens} s0={with_s0}")
+    dtype, dk, dv, H, lens, with_s0, with_dS = _case(seed)
+    _say(f"seed {seed}: {dtype} dk={dk} dv={dv} H={H} lens={lens} s0={with_s0} dS_final={with_dS}")
     cu = kda_inputs.cu_from_lengths(lens)
     T = int(cu[-1])
     x = kda_inputs.generate(500 + seed, T, H, dk, dv, dtype, num_seqs=len(lens), with_s0=with_s0, with_grads=True)
     d = {k: dev(x[k], dtype) for k in ("q", "k", "v", "g", "b", "dO")}
     cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
     s0 = torch.from_numpy(x["s0"]).cuda() if with_s0 else None
-    dS = torch.from_numpy(x["dS"]).cuda()
+    dS = torch.from_numpy(x["dS"]).cuda() if with_dS else None
     o, sf, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, save_for_bwd=True)
     gr = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS)
     torch.cuda.synchronize()
     o_ref, sf_ref = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu,
                                initial_state=x["s0"] if with_s0 else None)
     ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["b"], x["dO"], cu_seqlens=cu,
-                     initial_state=x["s0"] if with_s0 else None, dS_final=x["dS"])
+                     initial_state=x["s0"] if with_s0 else None, dS_final=x["dS"] if with_dS else None)
     bar, sbar = _bar(dtype)
     errs = {"o": _err(dtype, host(o), o_ref), "S_T": _err(dtype, host(sf), sf_ref, True)}
     for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "db")):
