@@ -59,13 +59,20 @@ kda_status check_config(const kda_config* c) {
     return KDA_OK;
 }
 
+// One launch covers at most 2^32 - 1 work-items along x (the dispatch packet's
+// grid size is a 32-bit count of work-items).
+bool grid_fits(int64_t workgroups, int threads) {
+    return workgroups >= 0 && workgroups * threads <= (int64_t)UINT32_MAX;
+}
+
 kda_status check_sizes(const kda_config* c, int64_t T, int32_t N, const int32_t* cu) {
     if (T < 0 || T >= ((int64_t)1 << 31)) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31)%s");
     if (N < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1%s");
     if (!cu && (T % N) != 0)
         return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is NULL but total_tokens is not a multiple of num_seqs%s");
-    if ((int64_t)N * c->H * (c->dv / kda::kSlice) >= ((int64_t)1 << 31))
-        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large%s");
+    if (!grid_fits((int64_t)N * c->H * (c->dv / kda::kSlice), kda::kWideThreads) ||
+        !grid_fits(kda::num_slots(T, N) * c->H, kda::kWideThreads))
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs, H or total_tokens too large for one launch%s");
     // the kernels address a chunk's rows with 32-bit offsets from a 64-bit base
     if ((int64_t)kda::kChunk * c->H * (c->dk > c->dv ? c->dk : c->dv) >= ((int64_t)1 << 31))
         return fail(KDA_ERR_UNSUPPORTED, "H too large%s");
@@ -272,8 +279,8 @@ kda_status kda_decode(const kda_config* cfg, int32_t N, const void* q, const voi
     g_err[0] = 0;
     KDA_TRY(check_config_common(cfg));
     if (N < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0%s");
-    if ((int64_t)N * cfg->H * (cfg->dv / kda::kSlice) >= ((int64_t)1 << 31))
-        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large%s");
+    if (!grid_fits((int64_t)N * cfg->H * (cfg->dv / kda::kSlice), kda::kThreads))
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H too large for one launch%s");
     if (N > 0) {
         KDA_TRY(need_ptr(q, "q"));
         KDA_TRY(need_ptr(k, "k"));

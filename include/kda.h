@@ -50,11 +50,15 @@
  *    [0, total_tokens) so it cannot address memory outside the buffers.
  *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
  *    {KDA_F32, KDA_BF16}, with fp32 inputs only at dk = 64 in kda_fwd and
- *    kda_bwd (KDA_ERR_UNSUPPORTED otherwise; kda_decode takes both dk); H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
- *    kernels address a chunk's rows with 32-bit offsets; KDA_ERR_UNSUPPORTED
- *    otherwise); total_tokens < 2^31; per-chunk cumulative
- *    log-decay sum_{chunk} g >= -80 per channel (the kernels factor
- *    exp(G_r - G_s) = exp(G_r) exp(-G_s) inside a 64-token chunk).
+ *    kda_bwd (kda_decode takes both dk); H >= 1 with
+ *    64 * H * max(dk, dv) < 2^31 (the kernels address a chunk's rows with
+ *    32-bit offsets); total_tokens < 2^31; one launch covers at most
+ *    2^32 - 1 work-items, so num_seqs * H * dv/64 and
+ *    (total_tokens/64 + num_seqs) * H stay below 2^23 (kda_decode:
+ *    num_seqs * H * dv/64 below 2^24).  Outside these, KDA_ERR_UNSUPPORTED.
+ *    Per-chunk cumulative log-decay sum_{chunk} g >= -80 per channel (the
+ *    kernels factor exp(G_r - G_s) = exp(G_r) exp(-G_s) inside a 64-token
+ *    chunk).
  */
 #ifndef KDA_H
 #define KDA_H

@@ -183,3 +183,14 @@ def test_head_count_bound():
     """64 * H * max(dk, dv) must stay below 2^31 (32-bit row offsets in a chunk)."""
     cfg = _lib.make_config(262144, 128, 128, KDA_BF16)       # 64 * 262144 * 128 = 2^31
     assert _fwd(cfg, T=64) == KDA_ERR_UNSUPPORTED and "H too large" in _err()
+
+
+def test_launch_size_bound():
+    """Every launch stays within 2^32 - 1 work-items along x; larger problems are refused on
+    the host (checked before any HIP call, so no device is needed)."""
+    many_docs = _lib.make_config(1, 64, 64, KDA_BF16)     # 2^23 one-token documents: 2^23 x 512 = 2^32
+    assert _fwd(many_docs, T=1 << 23, N=1 << 23) == KDA_ERR_UNSUPPORTED and "one launch" in _err()
+    many_chunks = _lib.make_config(1024, 64, 64, KDA_BF16)   # 8193 chunk slots x 1024 heads x 512 > 2^32 - 1
+    assert _fwd(many_chunks, T=1 << 19, N=1) == KDA_ERR_UNSUPPORTED and "one launch" in _err()
+    dec = _lib.make_config(1, 64, 64, KDA_BF16)            # 2^24 decode workgroups x 256 = 2^32
+    assert _decode(dec, N=1 << 24) == KDA_ERR_UNSUPPORTED and "one launch" in _err()
