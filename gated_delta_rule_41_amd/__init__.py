@@ -69,8 +69,9 @@ def _common(q, k, v, g, beta, cu_seqlens, num_seqs):
         _check(t, name, shp, dt, dev)
     _check(q, "q", (T, H, dk), dt, dev)
     if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the same device")
+        if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev
+                or not cu_seqlens.is_contiguous()):
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on the same device")
         N = cu_seqlens.numel() - 1
     else:
         N = 1 if num_seqs is None else int(num_seqs)
