@@ -4,7 +4,9 @@ The entry points enqueue kernels only (no allocation, no memset, no host
 synchronisation), so a serving loop or a training step can be captured once
 and replayed.  Each test captures a sequence of calls, replays the graph
 several times with eager work and synchronisations in between, and checks
-every replay bitwise against the same calls made eagerly.
+every replay bitwise against the same calls made eagerly.  A last test runs
+independent calls concurrently on three streams and checks them bitwise
+against the same calls made one after another.
 """
 import numpy as np
 import pytest
@@ -104,3 +106,61 @@ def test_forward_backward_in_a_graph():
         for name, a, r in zip(("o", "final_state") + names, outs, ref):
             assert torch.equal(a, r), (rep, name)
     _say("fwd+bwd replays bitwise equal to eager")
+
+
+def test_concurrent_streams_share_no_state():
+    """Three independent calls in flight at once on three streams (a training step, a
+    two-level long-sequence forward, decode steps) give bitwise the results of the same
+    calls made one after another: the library keeps no state between calls."""
+    need_gpu()
+    _say("concurrent streams: fwd+bwd, two-level forward, decode")
+    lens = [300, 64, 129]
+    cu = kda_inputs.cu_from_lengths(lens)
+    x = kda_inputs.generate(720, int(cu[-1]), 4, 128, 128, "bf16", num_seqs=len(lens), with_s0=True,
+                            with_grads=True)
+    a = {k: dev(x[k], "bf16") for k in ("q", "k", "v", "g", "b", "dO")}
+    cu_a = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0a = torch.from_numpy(x["s0"]).cuda()
+    dSa = torch.from_numpy(x["dS"]).cuda()
+    T_long = 40960                                    # one document, 2 heads: the library splits it
+    y = kda_inputs.generate(721, T_long, 2, 128, 128, "bf16", num_seqs=1, with_s0=True)
+    b = {k: dev(y[k], "bf16") for k in ("q", "k", "v", "g", "b")}
+    s0b = torch.from_numpy(y["s0"]).cuda()
+    z = kda_inputs.generate(722, 64, 8, 128, 128, "bf16", num_seqs=64, with_s0=True)
+    c = {k: dev(z[k], "bf16") for k in ("q", "k", "v", "g", "b")}
+    s0c = torch.from_numpy(z["s0"]).cuda()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+    def train():
+        o, sf, saved = kda.kda_fwd(a["q"], a["k"], a["v"], a["g"], a["b"], cu_a, s0a, save_for_bwd=True)
+        gr = kda.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["b"], saved, a["dO"], cu_a, s0a, dSa)
+        return [o, sf] + [gr[n] for n in names]
+
+    def long_fwd():
+        o, sf, _ = kda.kda_fwd(b["q"], b["k"], b["v"], b["g"], b["b"], None, s0b)
+        return [o, sf]
+
+    def decode():
+        st = s0c.clone()
+        outs = []
+        for t in range(4):   # the same token four times: the state moves on each step
+            o, st = kda.kda_decode(c["q"], c["k"], c["v"], c["g"], c["b"], st, out_state=st)
+            outs.append(o)
+        return outs + [st]
+
+    ref = [[r.clone() for r in f()] for f in (train, long_fwd, decode)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = []
+    for s, f in zip(streams, (train, long_fwd, decode)):
+        with torch.cuda.stream(s):
+            got.append(f())
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i, (g_list, r_list) in enumerate(zip(got, ref)):
+        for j, (g_t, r_t) in enumerate(zip(g_list, r_list)):
+            assert torch.equal(g_t, r_t), (i, j)
+    _say("concurrent results bitwise equal to sequential")
