@@ -693,6 +693,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             refresh();
             w_solve();
             lds_barrier();
+            // 5a and 5b: the compiler's MFMA/LDS interleaving pattern 1 (iglp_opt)
+            // schedules these two steps 2% faster than its default (measured;
+            // the same pattern made the forward's steps 4% slower)
+            __builtin_amdgcn_iglp_opt(1);
             // 5a: dU = Aqk^T dO + Ktil dS1
             refresh();
             V8T dof[2], duf[2];
@@ -730,6 +734,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     *reinterpret_cast<f32x4*>(at32(ub, vcol * kChunk + 16 * i + 4 * qg)) = dU[i];
             }
             lds_barrier();
+            __builtin_amdgcn_iglp_opt(1);
             // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
             refresh();
             const KtFrag kf2(qg, cl);
