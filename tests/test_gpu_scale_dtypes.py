@@ -172,3 +172,33 @@ def test_norm_eps_forward_backward_decode(dtype, dk, dv):
         assert errs[name] <= bar, (name, errs[name])
     # the default eps gives a visibly different output on these rows
     assert max_over_rms(host(o_def), o_ref) > 0.1
+
+
+def test_fp32_inputs_bf16_outputs():
+    """fp32 inputs with o and the gradients written in bf16: the same values as the fp32-output
+    call of the fp32-input kernels, beyond the storage rounding."""
+    need_gpu()
+    _say("fp32 inputs, bf16 outputs (forward and backward)")
+    lens = [130, 64, 1, 70]
+    cu = kda_inputs.cu_from_lengths(lens)
+    x = kda_inputs.generate(98, int(cu[-1]), 3, 64, 64, "f32", num_seqs=len(lens), with_s0=True, with_grads=True)
+    d = {k: dev(x[k], "f32") for k in ("q", "k", "v", "g", "b", "dO")}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    dS = torch.from_numpy(x["dS"]).cuda()
+    of, sff, saved = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, save_for_bwd=True)
+    ob, sfb, _ = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["b"], cu_t, s0, out_dtype=torch.bfloat16)
+    gf = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS)
+    gb = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["b"], saved, d["dO"], cu_t, s0, dS, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert ob.dtype == torch.bfloat16
+    assert torch.equal(sfb, sff)       # the final state is fp32 in both
+    e = _storage_excess(ob, of)
+    _say(f"  o: excess over bf16 storage {e:.2e}")
+    assert e <= SAME
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert gb[name].dtype == torch.bfloat16
+        e = _storage_excess(gb[name], gf[name])
+        _say(f"  {name}: excess over bf16 storage {e:.2e}")
+        assert e <= SAME, name
+    assert torch.equal(gb["dS0"], gf["dS0"])
