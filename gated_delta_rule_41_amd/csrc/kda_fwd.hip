@@ -557,28 +557,26 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
         const T* gc = gp + c0 * rs_k + h * DK;
         const T* vc = vp + c0 * rs_v + h * dv + dv0;
         const T* bc = bp + c0 * H + h;
-        const int ok = r0 * (int)rs_k + ck0, ov = r0 * (int)rs_v + VPL * cl, ob = r0 * H;
         const int sk = (int)rs_k, sv = (int)rs_v;
+        // Rows past the chunk end load the last row (in bounds) and are zeroed
+        // where they are first used (prep_a): no branch around the loads, and
+        // 32-bit unsigned offsets from the uniform bases.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (r0 + i < L) {
-                if (p0) {
-                    if (MAP) rq[i].zero();   // the maps need no queries
-                    else rq[i].load(qc + (ok + i * sk));
-                    rb[i].load(bc + (ob + i * H));
+            const int rc = min(r0 + i, L - 1);
+            const unsigned okr = (unsigned)(rc * sk + ck0);
+            if (p0) {
+                if (MAP) rq[i].zero();   // the maps need no queries
+                else rq[i].load(at32(qc, okr));
+                rb[i].load(at32(bc, (unsigned)(rc * H)));
+            }
+            if (p1) rk[i].load(at32(kc, okr));
+            if (p2) {
+                rg[i].load(at32(gc, okr));
+                if (!is_state) {
+                    if (mslice) rv[i].zero();
+                    else rv[i].load(at32(vc, (unsigned)(rc * sv + VPL * cl)));
                 }
-                if (p1) rk[i].load(kc + (ok + i * sk));
-                if (p2) {
-                    rg[i].load(gc + (ok + i * sk));
-                    if (!is_state) {
-                        if (mslice) rv[i].zero();
-                        else rv[i].load(vc + (ov + i * sv));
-                    }
-                }
-            } else {
-                if (p0) { rq[i].zero(); rb[i].zero(); }
-                if (p1) rk[i].zero();
-                if (p2) { rg[i].zero(); rv[i].zero(); }
             }
         }
         if (p0) Lp = L;
@@ -599,6 +597,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd_bf16_kernel(FwdParams
     // first half of the prep: this half's sums of squares, sigmoid, the wave's
     // gate column sums
     auto prep_a = [&]() {
+        if (Lp < kChunk) {   // uniform: the last chunk of a document zeroes its rows past the end
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = r0 + i < Lp;
+                rq[i].keep(ok); rk[i].keep(ok); rg[i].keep(ok);
+                if (!is_state) rv[i].keep(ok);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sq = 0.f, sk = 0.f;
