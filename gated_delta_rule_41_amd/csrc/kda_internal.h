@@ -128,6 +128,9 @@ hipError_t launch_decode(const DecodeParams& p, int in_dtype, int out_dtype, int
 // Two-level forward pieces (bf16 inputs): segment split, segment maps, carry scan.
 hipError_t launch_segments(const SegParams& p, hipStream_t stream);
 hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t stream);
+// bf16 inputs: the fused forward with fp16 matrix-core operands (kda_fwd16.hip).
+hipError_t launch_fwd16(const FwdParams& p, int out_dtype, int dk, bool save, hipStream_t stream);
+hipError_t launch_fwd16_maps(const FwdParams& p, int dk, hipStream_t stream);
 hipError_t launch_carry(const CarryParams& p, int dk, hipStream_t stream);
 
 }  // namespace kda

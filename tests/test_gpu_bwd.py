@@ -100,10 +100,17 @@ def test_bwd_deterministic_and_adjoint():
     torch.cuda.synchronize()
     for k in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
         assert torch.equal(gr[k], st[k]), ("stages", k)
+    ov, dOv = host(o).astype(np.float64), x["dO"].astype(np.float64)
     lhs = float((host(gr["dv"]) * x["v"]).sum() + (host(gr["dS0"]) * x["s0"]).sum())
-    rhs = float((host(o) * x["dO"]).sum() + (host(sf) * x["dS"]).sum())
-    _say(f"adjoint lhs={lhs:.6e} rhs={rhs:.6e}")
-    assert abs(lhs - rhs) <= 1e-3 * (abs(lhs) + abs(rhs))
+    rhs = float((ov * dOv).sum() + (host(sf) * x["dS"]).sum())
+    # Both sides are sums of ~5e5 terms of either sign whose result is a small
+    # residual, so a bound relative to the result does not follow from the
+    # per-element bar.  Bound: every o off by 2e-2 rms(o) in a direction
+    # unrelated to dO moves <dO, o> by about 2e-2 rms(o) |dO|_2 (and the
+    # gradients' side likewise).  A wrong gradient formula moves it by O(|rhs|).
+    tol = 2e-2 * np.sqrt(np.mean(ov * ov)) * np.linalg.norm(dOv)
+    _say(f"adjoint lhs={lhs:.6e} rhs={rhs:.6e} tol={tol:.3e}")
+    assert abs(lhs - rhs) <= tol
 
 
 def test_bwd_w2_sampled_heads():
