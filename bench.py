@@ -103,9 +103,9 @@ FWD_GRID = 4 * 32 * 2 * 512   # threads in one launch of the workload's fused fo
 KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file, grid size or None)
     "grads": ("kda_bwd_grads_kernel<float, 128, 128>", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
     "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
-    "fwd": ("kda_fwd_bf16_kernel<float, 128, true, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip", FWD_GRID),
+    "fwd": ("kda_fwd16_kernel<float, 128, true, false>", "gated_delta_rule_41_amd/csrc/kda_fwd16.hip", FWD_GRID),
     # the long-context run's second level launches the same kernel on another grid
-    "fwd_infer": ("kda_fwd_bf16_kernel<float, 128, false, false>", "gated_delta_rule_41_amd/csrc/kda_fwd.hip",
+    "fwd_infer": ("kda_fwd16_kernel<float, 128, false, false>", "gated_delta_rule_41_amd/csrc/kda_fwd16.hip",
                   FWD_GRID),
     "decode": ("kda_decode_kernel", "gated_delta_rule_41_amd/csrc/kda_decode.hip", None),
 }
@@ -404,7 +404,7 @@ def main():
     del lq, lk, lv, lg, lb, ls0
 
     tokens = B * T
-    names = {"fwd": "kda_fwd_bf16_kernel (training forward, state save)",
+    names = {"fwd": "kda_fwd16_kernel (training forward, state save)",
              "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
              "grads": "kda_bwd_grads_kernel (chunk-parallel gradients)"}
     dom = max(kms, key=kms.get)
@@ -437,7 +437,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": ach, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                      "traffic": traffic, "alg_bytes_per_launch": dbytes, "ms_per_launch": kms[dom]},
-        "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd_bf16_kernel (inference, no save)",
+        "roofline_fwd": {"bound": "hbm", "kernel": "kda_fwd16_kernel (inference, no save)",
                          "achieved": f_bytes / (inf_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": f_bytes / (inf_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": traffic_record("fwd_infer"), "alg_bytes_per_launch": f_bytes,

@@ -84,15 +84,18 @@ __device__ __forceinline__ void cvt_store(h16* dst, const float (&x)[N]) {
     *reinterpret_cast<HV*>(dst) = __builtin_convertvector(v, HV);
 }
 
-// Wave-wide maximum (every lane gets it).
+// Wave-wide maximum of non-negative values, as a wave-uniform value: DPP
+// within each 16-lane row, then the four row results.
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 32));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 8));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 1));
-    return v;
+    v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 // Sum over the four lanes that share l % 16 (l, l^16, l^32, l^48): every one
 // of them gets the same bits.
@@ -104,7 +107,7 @@ __device__ __forceinline__ float qsum(float v) {
 constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
 template <int DK>
-struct Smem {
+struct __attribute__((aligned(16))) Smem {
     static constexpr int PK = DK + 8;      // row stride of [64][DK] tiles (halfs)
     static constexpr int PC = kChunk + 8;  // row stride of [64][64] tiles
     static constexpr int PV = kChunk + 8;  // row stride of the transposed v tile
@@ -124,6 +127,7 @@ struct Smem {
         int flag[4];              // per prep wave: the chunk breaks the fp16 gate bound
     } buf[2];
     float etot[4][DK];            // 2^(block decay) per 16-row block
+    h16 etoth[4][DK];             //   the same in fp16
     h16 kcol[3][16 * PK];         // blocks 0-2: kh 2^(G_b - G) (column operands), fragment order
 };
 
@@ -282,14 +286,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[mb][i]));
-                    ms = wave_max(ms);
-                    mv = wave_max(mv);
-                    constexpr int kNone = -100000;
-                    int Es = kNone, Ev = kNone;
-                    if (ms > 0.f && ms < __builtin_inff()) { frexpf(ms, &Es); Es += e; }
-                    if (mv > 0.f && mv < __builtin_inff()) frexpf(mv, &Ev);
-                    const int Et = __builtin_amdgcn_readfirstlane(Es > Ev ? Es : Ev);
-                    if (Et != kNone) {
+                    // the largest |state| (true scale, exact) or |v|
+                    const float m = wave_max(fmaxf(ms * usc, mv));
+                    if (m > 0.f && m < __builtin_inff()) {
+                        int Et;
+                        frexpf(m, &Et);   // m in [2^(Et-1), 2^Et)
                         const int en = min(max(Et - 6, -100), 100);
                         const int d = en - e;
                         if (d != 0) {
@@ -441,22 +442,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
         RawRow<T, CPG> rg[4];              // gate rows 16pw+4qg+j, channels CPG*cl ..
         RawRow<T, 4> rv[4];                // v rows 16pw+4qg+j, slice columns 4cl ..
         RawScalar<T> rb;
-        int Lm = 0;
-        auto load_rows = [&](int64_t c0) {
-            const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-            const T* qc = qp + c0 * rs_k + h * DK;
-            const T* kc = kp + c0 * rs_k + h * DK;
+        // next-chunk rows go out in two groups, each as soon as its registers
+        // are free: gates, beta and v after the gate prefix, q and k after the
+        // diagonal-block products
+        auto chunk_len = [&](int64_t c0) { return (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk); };
+        auto load_gbv = [&](int64_t c0) {
+            const int L = chunk_len(c0);
             const T* gc = gp + c0 * rs_k + h * DK;
             const T* vc = vp + c0 * rs_v + h * dv + dv0;
             const T* bc = bp + c0 * H + h;
             const int sk = (int)rs_k, sv = (int)rs_v;
             // rows past the chunk end load the last row (in bounds) and are
             // zeroed where first used
-            const int r = min(rr, L - 1);
-            if (MAP) rq.zero();
-            else rq.load(at32(qc, (unsigned)(r * sk + CPL * qg)));
-            rk.load(at32(kc, (unsigned)(r * sk + CPL * qg)));
-            rb.load(at32(bc, (unsigned)(r * H)));
+            rb.load(at32(bc, (unsigned)(min(rr, L - 1) * H)));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rj = min(16 * pw + 4 * qg + j, L - 1);
@@ -464,9 +462,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 if (mslice) rv[j].zero();
                 else rv[j].load(at32(vc, (unsigned)(rj * sv + 4 * cl)));
             }
-            Lm = L;
         };
-        if (nch > 0) load_rows(t0);
+        auto load_qk = [&](int64_t c0) {
+            const int L = chunk_len(c0);
+            const T* qc = qp + c0 * rs_k + h * DK;
+            const T* kc = kp + c0 * rs_k + h * DK;
+            const int sk = (int)rs_k;
+            const int r = min(rr, L - 1);
+            if (MAP) rq.zero();
+            else rq.load(at32(qc, (unsigned)(r * sk + CPL * qg)));
+            rk.load(at32(kc, (unsigned)(r * sk + CPL * qg)));
+        };
+        if (nch > 0) {
+            load_gbv(t0);
+            load_qk(t0);
+        }
 
         for (int it = -1; it <= nch; ++it) {
             const int m = it + 1;              // chunk prepared in this iteration
@@ -484,7 +494,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
             h8 Rq[NKB], Rk[NKB], Cd[NKB];
             f32x4 d3 = {0.f, 0.f, 0.f, 0.f};
             if (act) {
-                if (__builtin_amdgcn_readfirstlane(Lm) < kChunk) {
+                const int Lm = __builtin_amdgcn_readfirstlane(chunk_len(cm));
+                const bool more = m + 1 < nch;
+                if (Lm < kChunk) {
                     // the last chunk of a document: rows past its end are zero
                     const bool rok = rr < Lm;
                     rq.keep(rok);
@@ -497,6 +509,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         rv[j].keep(ok);
                     }
                 }
+                // v transposed (bf16 bits) for the state waves
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) {
+                    const u16x4 x = {rv[0].x[ee], rv[1].x[ee], rv[2].x[ee], rv[3].x[ee]};
+                    *reinterpret_cast<u16x4*>(&B.vt[(4 * cl + ee) * PV + 16 * pw + 4 * qg]) = x;
+                }
                 float sq = 0.f, sk = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
@@ -508,6 +526,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 // (the query scale is applied to O, which is linear in qh)
                 const float rqs = 1.f / nq, rkk = 1.f / nk;
                 const float beta = (rr < Lm) ? 1.f / (1.f + fast_exp(-rb.f())) : 0.f;
+                if (qg == 0) B.beta[rr] = beta;
                 // block-local inclusive prefix of g over the wave's 16 rows, as one
                 // k16 product per column group (exact bf16 products, fp32 sums); it
                 // returns lane (qg, cl) row 16pw+cl, channels CPG*(4qg+i)+e
@@ -550,8 +569,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     x.x = fast_exp2(x.x);
                     x.y = fast_exp2(x.y);
                     __builtin_amdgcn_wave_barrier();
-                    if (2 * l < DK) *e2 = x;
+                    if (2 * l < DK) {
+                        *e2 = x;
+                        *reinterpret_cast<hx2*>(&sm.etoth[pw][2 * l]) = __builtin_convertvector(f2{x.x, x.y}, hx2);
+                    }
                 }
+                // gates, beta and v are used up
+                asm volatile("" ::: "memory");
+                if (more) load_gbv(cm + kChunk);
                 // operands referenced at the block start: rows x 2^Gl (<= 1),
                 // columns kh 2^-Gl (<= 2^14), and the diagonal-block products
                 f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
@@ -573,6 +598,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     if constexpr (pw < 3)
                         *reinterpret_cast<h8*>(&sm.kcol[pw][cl * PK + CPL * qg + 8 * kk]) = Cd[kk];
                 }
+                // q and k are used up
+                asm volatile("" ::: "memory");
+                if (more) load_qk(cm + kChunk);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int sI = 4 * qg + i;
@@ -602,20 +630,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     const f32x4 tt = mma16(z, cvt4(zz), cvt4(eyev - d1));   // (I-N)^T
                     *reinterpret_cast<h4*>(&B.td[pw][cl * TDS + 4 * qg]) = cvt4(tt);
                 }
-                // v transposed (bf16 bits) and beta for the state waves
-#pragma unroll
-                for (int ee = 0; ee < 4; ++ee) {
-                    const u16x4 x = {rv[0].x[ee], rv[1].x[ee], rv[2].x[ee], rv[3].x[ee]};
-                    *reinterpret_cast<u16x4*>(&B.vt[(4 * cl + ee) * PV + 16 * pw + 4 * qg]) = x;
-                }
-                if (qg == 0) B.beta[rr] = beta;
                 if (SAVE && slice == 0 && qg == 0 && rr < Lm) {
                     p.nq_saved[(cm + rr) * H + h] = nq;
                     p.nk_saved[(cm + rr) * H + h] = nk;
                 }
-                // the raw rows are used up: fetch the next chunk
-                asm volatile("" ::: "memory");
-                if (m + 1 < nch) load_rows(cm + kChunk);
             }
             lds_barrier();
             // --------------------------------------------------------- phase B
@@ -634,20 +652,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 f32x4 aoff[3][2];
 #pragma unroll
                 for (int jb = 0; jb < 3; ++jb) aoff[jb][0] = aoff[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // identity halves for the Ktil transpose: B[k = 8qg+j][n = cl] = (k == n + 16hh)
+                h8 eye[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) eye[hh][j] = (h16)((8 * qg + j == cl + 16 * hh) ? 1.f : 0.f);
+                h8 aqs[2], aks[2];   // (dk = 128) fragments 0 and 1, written beside 2 and 3
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk) {
                     // the four blocks' decays of these 8 channels, in fp16 (each is
                     // >= 2^-14 on this path); in every product below a factor that
                     // may underflow is the last one, so what it makes tiny is tiny
                     h8 E[4];
-                    f32x4 e32[4][2];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf)
-                            e32[b][hf] = *reinterpret_cast<const f32x4*>(&sm.etot[b][CPL * qg + 8 * kk + 4 * hf]);
-                        E[b] = cvt8(e32[b][0], e32[b][1]);
-                    }
+                    for (int b = 0; b < 4; ++b) E[b] = *reinterpret_cast<const h8*>(&sm.etoth[b][CPL * qg + 8 * kk]);
                     h8 eoff = (h8)(h16)1.f, eaft = (h8)(h16)1.f;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
@@ -655,33 +674,50 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         if (b > pw) eaft = eaft * E[b];
                     }
                     const h8 aq = Rq[kk] * eoff;                 // qh 2^G
-                    const h8 ak = -(Rk[kk] * eoff);              // -beta kh 2^G
+                    const h8 ak = Rk[kk] * (-eoff);              // -beta kh 2^G
                     const h8 kt8 = (Cd[kk] * E[pw]) * eaft;      // kh 2^(G_C - G)
                     // qh 2^G, -beta kh 2^G (contraction index permuted: position
-                    // 8q'+4hh+j of a 32-block holds channel 16hh+4q'+j), two
-                    // 4-channel pieces
+                    // 8q'+4hh+j of a 32-block holds channel 16hh+4q'+j)
+                    if constexpr (DK == 128) {
+                        if (kk < 2) {
+                            aqs[kk] = aq;
+                            aks[kk] = ak;
+                        } else {
+                            // 16-byte groups 8(kk-2) and 8(kk-2)+8 of the lane's 32-block:
+                            // channels {4u..4u+3} of fragment kk-2 beside {16+4u..} of kk
 #pragma unroll
-                    for (int u2 = 0; u2 < 2; ++u2) {
-                        const int u = 2 * kk + u2;
-                        int pos;
-                        if constexpr (DK == 128) pos = 32 * qg + 8 * (u & 3) + 4 * (u >> 2);
-                        else pos = 32 * (qg >> 1) + 4 * (qg & 1) + 8 * u;
-                        h4 a, b;
+                            for (int u2 = 0; u2 < 2; ++u2) {
+                                const int pos = 32 * qg + 8 * (2 * (kk - 2) + u2);
+                                h8 a, b;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) { a[j] = aq[4 * u2 + j]; b[j] = ak[4 * u2 + j]; }
-                        if (!MAP) *reinterpret_cast<h4*>(dq + pos) = a;
-                        *reinterpret_cast<h4*>(dk + pos) = b;
+                                for (int j = 0; j < 4; ++j) {
+                                    a[j] = aqs[kk - 2][4 * u2 + j];
+                                    a[j + 4] = aq[4 * u2 + j];
+                                    b[j] = aks[kk - 2][4 * u2 + j];
+                                    b[j + 4] = ak[4 * u2 + j];
+                                }
+                                if (!MAP) *reinterpret_cast<h8*>(dq + pos) = a;
+                                *reinterpret_cast<h8*>(dk + pos) = b;
+                            }
+                        }
+                    } else {
+                        // 16 channels: half hh = qg & 1 of the 32-block qg >> 1
+#pragma unroll
+                        for (int u2 = 0; u2 < 2; ++u2) {
+                            const int pos = 32 * (qg >> 1) + 4 * (qg & 1) + 8 * (2 * kk + u2);
+                            h4 a, b;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) { a[j] = aq[4 * u2 + j]; b[j] = ak[4 * u2 + j]; }
+                            if (!MAP) *reinterpret_cast<h4*>(dq + pos) = a;
+                            *reinterpret_cast<h4*>(dk + pos) = b;
+                        }
                     }
                     // Ktil^T through the matrix core: A = this lane's Ktil fragment,
-                    // B = an identity half (B[k = 8qg+j][n = cl] = (k == n + 16hh)),
-                    // so lane (qg', cl') receives rows 16pw+4qg'+i of the channel in
-                    // k-slot cl'+16hh
+                    // B = an identity half, so lane (qg', cl') receives rows
+                    // 16pw+4qg'+i of the channel in k-slot cl'+16hh
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        h8 eye;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) eye[j] = (h16)((8 * qg + j == cl + 16 * hh) ? 1.f : 0.f);
-                        const f32x4 d = mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kt8, eye);
+                        const f32x4 d = mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kt8, eye[hh]);
                         const int ks = cl + 16 * hh;
                         const int c = CPL * (ks >> 3) + 8 * kk + (ks & 7);
                         *reinterpret_cast<h4*>(&B.kt[kt_off(c, perm32(16 * pw + 4 * qg))]) = cvt4(d);
@@ -700,9 +736,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         if (cl == 0) {
                             // 2^G_C in fp32 (it scales the fp32 state)
 #pragma unroll
-                            for (int hf = 0; hf < 2; ++hf)
-                                *reinterpret_cast<f32x4*>(&B.gamc[CPL * qg + 8 * kk + 4 * hf]) =
-                                    e32[0][hf] * e32[1][hf] * e32[2][hf] * e32[3][hf];
+                            for (int hf = 0; hf < 2; ++hf) {
+                                f32x4 gc = *reinterpret_cast<const f32x4*>(&sm.etot[0][CPL * qg + 8 * kk + 4 * hf]);
+#pragma unroll
+                                for (int b = 1; b < 4; ++b)
+                                    gc *= *reinterpret_cast<const f32x4*>(&sm.etot[b][CPL * qg + 8 * kk + 4 * hf]);
+                                *reinterpret_cast<f32x4*>(&B.gamc[CPL * qg + 8 * kk + 4 * hf]) = gc;
+                            }
                         }
                     }
                     // keep the next group's LDS reads behind this group's work
