@@ -101,7 +101,8 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: 
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.kda_fwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                    _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(saved), _ptr(ws), wsb, stream))
+                                    _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(saved),
+                                    0 if saved is None else saved.numel(), _ptr(ws), wsb, stream))
     return o, sf, saved
 
 
@@ -145,7 +146,7 @@ def kda_bwd(q, k, v, g, beta, saved, dO, cu_seqlens=None, initial_state=None, dS
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.kda_bwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                    _ptr(initial_state), _ptr(saved), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
+                                    _ptr(initial_state), _ptr(saved), saved.numel(), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
                                     _ptr(out["dS0"]), _ptr(ws), wsb, stream, stage))
     return out

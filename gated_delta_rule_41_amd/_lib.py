@@ -67,11 +67,13 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32]
         fn.restype = ctypes.c_size_t
-    lib.kda_fwd.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+    lib.kda_fwd.argtypes = ([cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
+                            + [ctypes.c_size_t, _vp])
     lib.kda_fwd.restype = ctypes.c_int
     for name in ("kda_bwd", "kda_bwd_scan", "kda_bwd_grads"):
         fn = getattr(lib, name)
-        fn.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 17 + [ctypes.c_size_t, _vp]
+        fn.argtypes = ([cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 8 + [ctypes.c_size_t] + [_vp] * 9
+                       + [ctypes.c_size_t, _vp])
         fn.restype = ctypes.c_int
     lib.kda_decode.argtypes = [cfgp, ctypes.c_int32] + [_vp] * 9
     lib.kda_decode.restype = ctypes.c_int
@@ -112,23 +114,23 @@ def kda_bwd_workspace_size(cfg: KdaConfig, total_tokens: int, num_seqs: int) -> 
 
 
 def kda_fwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, o,
-                final_state, saved, workspace, workspace_bytes, stream) -> int:
+                final_state, saved, saved_bytes, workspace, workspace_bytes, stream) -> int:
     """Direct call of kda_fwd with integer device addresses (0 = NULL); returns the status."""
     return load().kda_fwd(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens,
-                          initial_state, o, final_state, saved, workspace, workspace_bytes, stream)
+                          initial_state, o, final_state, saved, saved_bytes, workspace, workspace_bytes, stream)
 
 
 BWD_ENTRY = {"all": "kda_bwd", "scan": "kda_bwd_scan", "grads": "kda_bwd_grads"}
 
 
-def kda_bwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved,
+def kda_bwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved, saved_bytes,
                 dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes,
                 stream, stage: str = "all") -> int:
     """Direct call of kda_bwd (stage "all"), kda_bwd_scan ("scan") or kda_bwd_grads
     ("grads") with integer device addresses (0 = NULL); returns the status."""
     fn = getattr(load(), BWD_ENTRY[stage])
     return fn(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, saved,
-              dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream)
+              saved_bytes, dO, dS_final, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream)
 
 
 def kda_decode_raw(cfg, num_seqs, q, k, v, g, beta, state_in, state_out, o, stream) -> int:

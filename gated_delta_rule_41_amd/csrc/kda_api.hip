@@ -160,6 +160,88 @@ size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
     return align256((size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c));
 }
 
+// Every argument check of kda_fwd except the workspace's.
+kda_status fwd_check(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k, const void* v,
+                     const void* g, const void* beta, const int32_t* cu, const float* s0, const void* o,
+                     const float* sfinal, const void* saved, size_t saved_bytes) {
+    KDA_TRY_(check_config(cfg));
+    KDA_TRY_(check_sizes(cfg, T, N, cu));
+    if (T > 0) {
+        KDA_TRY_(need_ptr(q, "q"));
+        KDA_TRY_(need_ptr(k, "k"));
+        KDA_TRY_(need_ptr(v, "v"));
+        KDA_TRY_(need_ptr(g, "g"));
+        KDA_TRY_(need_ptr(beta, "beta"));
+        KDA_TRY_(need_ptr(o, "o"));
+    }
+    KDA_TRY_(opt_ptr(cu, "cu_seqlens"));
+    KDA_TRY_(opt_ptr(s0, "initial_state"));
+    KDA_TRY_(opt_ptr(sfinal, "final_state"));
+    if (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) {
+        KDA_TRY_(need_ptr(saved, "saved"));
+        if (saved_bytes < kda_saved_size(cfg, T, N)) return fail(KDA_ERR_WORKSPACE, "saved buffer too small%s");
+    }
+    return KDA_OK;
+}
+
+// The forward's launches, after every check; `workspace` holds at least
+// kda_fwd_workspace_size() bytes.
+kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k, const void* v,
+                      const void* g, const void* beta, const int32_t* cu, const float* s0, void* o,
+                      float* sfinal, void* saved, void* workspace, hipStream_t st) {
+    const bool save = (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) != 0;
+    kda::FwdParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.b = beta;
+    p.cu = cu; p.s0 = s0; p.o = o; p.sfinal = sfinal;
+    if (save) {
+        const SavedLayout L = saved_layout(cfg, T, N);
+        char* base = (char*)saved;
+        p.st_saved = base + L.states;
+        p.nq_saved = (float*)(base + L.nq);
+        p.nk_saved = (float*)(base + L.nk);
+        p.u_saved = chunk_u_bytes(cfg, T, N) ? (float*)(base + L.u) : nullptr;
+    }
+    p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
+    p.seqlen = cu ? 0 : (int32_t)(T / N);
+    p.eps = cfg->l2_eps; p.scale = cfg->scale;
+    p.nslices = cfg->dv / kda::kSlice;
+    const SplitPlan sp = split_plan(cfg, T, N);
+    hipError_t e = hipSuccess;
+    if (!sp.on) {
+        e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, st);
+    } else {
+        char* ws = (char*)workspace;
+        int32_t* seg_cu = (int32_t*)(ws + sp.seg_cu);
+        int32_t* doc_seg = (int32_t*)(ws + sp.doc_seg);
+        int32_t* sf_dst = (int32_t*)(ws + sp.sf_dst);
+        float* maps = (float*)(ws + sp.maps);
+        float* s_in = (float*)(ws + sp.s_in);
+        kda::SegParams sg = {cu, seg_cu, doc_seg, sf_dst, T, N, p.seqlen, sp.seg_len, sp.P};
+        e = kda::launch_segments(sg, st);
+        if (e == hipSuccess) {   // every segment's [M | B] from the zero state
+            kda::FwdParams pm = p;
+            pm.cu = seg_cu; pm.N = sp.P; pm.seqlen = 0;
+            pm.s0 = nullptr; pm.o = nullptr; pm.sfinal = maps; pm.sf_dst = nullptr;
+            pm.nslices = (cfg->dk + cfg->dv) / kda::kSlice;
+            pm.map_slices = cfg->dk / kda::kSlice;
+            e = kda::launch_fwd_maps(pm, cfg->dk, st);
+        }
+        if (e == hipSuccess) {   // the state entering every segment
+            kda::CarryParams cp = {doc_seg, s0, maps, s_in, N, cfg->H, cfg->dv, cfg->dv / kda::kSlice};
+            e = kda::launch_carry(cp, cfg->dk, st);
+        }
+        if (e == hipSuccess) {   // the segments from their entering states
+            kda::FwdParams pc = p;
+            pc.cu = seg_cu; pc.N = sp.P; pc.seqlen = 0;
+            pc.s0 = s_in; pc.sf_dst = sf_dst;
+            e = kda::launch_fwd(pc, cfg->in_dtype, cfg->out_dtype, cfg->dk, false, st);
+        }
+    }
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
 }  // namespace
 
 #define KDA_TRY(x) KDA_TRY_(x)
@@ -197,80 +279,15 @@ size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
 
 kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
                    const void* v, const void* g, const void* beta, const int32_t* cu,
-                   const float* s0, void* o, float* sfinal, void* saved, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   const float* s0, void* o, float* sfinal, void* saved, size_t saved_bytes,
+                   void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
-    KDA_TRY(check_config(cfg));
-    KDA_TRY(check_sizes(cfg, T, N, cu));
-    if (T > 0) {
-        KDA_TRY(need_ptr(q, "q"));
-        KDA_TRY(need_ptr(k, "k"));
-        KDA_TRY(need_ptr(v, "v"));
-        KDA_TRY(need_ptr(g, "g"));
-        KDA_TRY(need_ptr(beta, "beta"));
-        KDA_TRY(need_ptr(o, "o"));
-    }
-    KDA_TRY(opt_ptr(cu, "cu_seqlens"));
-    KDA_TRY(opt_ptr(s0, "initial_state"));
-    KDA_TRY(opt_ptr(sfinal, "final_state"));
+    KDA_TRY(fwd_check(cfg, T, N, q, k, v, g, beta, cu, s0, o, sfinal, saved, saved_bytes));
     KDA_TRY(opt_ptr(workspace, "workspace"));
-    const bool save = (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) != 0;
-    if (save) KDA_TRY(need_ptr(saved, "saved"));
     const size_t ws_need = kda_fwd_workspace_size(cfg, T, N);
     if (workspace_bytes < ws_need) return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
     if (ws_need > 0) KDA_TRY(need_ptr(workspace, "workspace"));
-
-    kda::FwdParams p;
-    memset(&p, 0, sizeof p);
-    p.q = q; p.k = k; p.v = v; p.g = g; p.b = beta;
-    p.cu = cu; p.s0 = s0; p.o = o; p.sfinal = sfinal;
-    if (save) {
-        const SavedLayout L = saved_layout(cfg, T, N);
-        char* base = (char*)saved;
-        p.st_saved = base + L.states;
-        p.nq_saved = (float*)(base + L.nq);
-        p.nk_saved = (float*)(base + L.nk);
-        p.u_saved = chunk_u_bytes(cfg, T, N) ? (float*)(base + L.u) : nullptr;
-    }
-    p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
-    p.seqlen = cu ? 0 : (int32_t)(T / N);
-    p.eps = cfg->l2_eps; p.scale = cfg->scale;
-    p.nslices = cfg->dv / kda::kSlice;
-    const SplitPlan sp = split_plan(cfg, T, N);
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = hipSuccess;
-    if (!sp.on) {
-        e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, st);
-    } else {
-        char* ws = (char*)workspace;
-        int32_t* seg_cu = (int32_t*)(ws + sp.seg_cu);
-        int32_t* doc_seg = (int32_t*)(ws + sp.doc_seg);
-        int32_t* sf_dst = (int32_t*)(ws + sp.sf_dst);
-        float* maps = (float*)(ws + sp.maps);
-        float* s_in = (float*)(ws + sp.s_in);
-        kda::SegParams sg = {cu, seg_cu, doc_seg, sf_dst, T, N, p.seqlen, sp.seg_len, sp.P};
-        e = kda::launch_segments(sg, st);
-        if (e == hipSuccess) {   // every segment's [M | B] from the zero state
-            kda::FwdParams pm = p;
-            pm.cu = seg_cu; pm.N = sp.P; pm.seqlen = 0;
-            pm.s0 = nullptr; pm.o = nullptr; pm.sfinal = maps; pm.sf_dst = nullptr;
-            pm.nslices = (cfg->dk + cfg->dv) / kda::kSlice;
-            pm.map_slices = cfg->dk / kda::kSlice;
-            e = kda::launch_fwd_maps(pm, cfg->dk, st);
-        }
-        if (e == hipSuccess) {   // the state entering every segment
-            kda::CarryParams cp = {doc_seg, s0, maps, s_in, N, cfg->H, cfg->dv, cfg->dv / kda::kSlice};
-            e = kda::launch_carry(cp, cfg->dk, st);
-        }
-        if (e == hipSuccess) {   // the segments from their entering states
-            kda::FwdParams pc = p;
-            pc.cu = seg_cu; pc.N = sp.P; pc.seqlen = 0;
-            pc.s0 = s_in; pc.sf_dst = sf_dst;
-            e = kda::launch_fwd(pc, cfg->in_dtype, cfg->out_dtype, cfg->dk, false, st);
-        }
-    }
-    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return KDA_OK;
+    return fwd_launch(cfg, T, N, q, k, v, g, beta, cu, s0, o, sfinal, saved, workspace, (hipStream_t)stream);
 }
 
 kda_status kda_decode(const kda_config* cfg, int32_t N, const void* q, const void* k, const void* v,
@@ -311,7 +328,8 @@ kda_status kda_decode(const kda_config* cfg, int32_t N, const void* q, const voi
 
 static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t N, const void* q,
                            const void* k, const void* v, const void* g, const void* beta, const int32_t* cu,
-                           const float* s0, const void* saved, const void* dO, const float* dSf, void* dq,
+                           const float* s0, const void* saved, size_t saved_bytes, const void* dO,
+                           const float* dSf, void* dq,
                            void* dk, void* dv, void* dg, void* dbeta, float* dS0, void* workspace,
                            size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
@@ -331,6 +349,7 @@ static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t
         KDA_TRY(need_ptr(dbeta, "dbeta"));
     }
     KDA_TRY(need_ptr(saved, "saved"));
+    if (saved_bytes < kda_saved_size(cfg, T, N)) return fail(KDA_ERR_WORKSPACE, "saved buffer too small%s");
     KDA_TRY(opt_ptr(cu, "cu_seqlens"));
     KDA_TRY(opt_ptr(s0, "initial_state"));
     KDA_TRY(opt_ptr(dSf, "dS_final"));
@@ -366,10 +385,11 @@ static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t
 
 #define KDA_BWD_ARGS                                                                                   \
     const kda_config *cfg, int64_t T, int32_t N, const void *q, const void *k, const void *v, const void *g, \
-        const void *beta, const int32_t *cu, const float *s0, const void *saved, const void *dO,          \
+        const void *beta, const int32_t *cu, const float *s0, const void *saved, size_t saved_bytes,      \
+        const void *dO,                                                                                   \
         const float *dSf, void *dq, void *dk, void *dv, void *dg, void *dbeta, float *dS0, void *workspace, \
         size_t workspace_bytes, void *stream
-#define KDA_BWD_PASS cfg, T, N, q, k, v, g, beta, cu, s0, saved, dO, dSf, dq, dk, dv, dg, dbeta, dS0, workspace, \
+#define KDA_BWD_PASS cfg, T, N, q, k, v, g, beta, cu, s0, saved, saved_bytes, dO, dSf, dq, dk, dv, dg, dbeta, dS0, workspace, \
                      workspace_bytes, stream
 
 kda_status kda_bwd(KDA_BWD_ARGS) { return bwd_call(kda::kBwdScan | kda::kBwdGrads, KDA_BWD_PASS); }

@@ -1044,7 +1044,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // g, which the first call leaves in LDS.
     struct Prep {
         RawRow<T, CPH> q[4], k[4];
-        float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4];
+        float G[4][CPH], GC[CPH], beta[4], dsig[4], iq[4], ik[4];
     };
     // after_loads runs once the row loads are issued, before their first use:
     // more loads issued there wait only behind these
@@ -1070,6 +1070,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             P.q[i].keep(ok); P.k[i].keep(ok); rg[i].keep(ok);
             // v_rcp (~1 ulp), as the forward forms beta and the reciprocal norms
             P.beta[i] = ok ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
+            P.dsig[i] = ok ? sigmoid_deriv(rb[i]) : 0.f;
             P.iq[i] = p.scale * __builtin_amdgcn_rcpf(ok ? nq[i] : 1.f);
             P.ik[i] = __builtin_amdgcn_rcpf(ok ? nk[i] : 1.f);
         }
@@ -1637,7 +1638,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             if (wh == 0 && cl == 0) {
                 const float db = srow[2 * 64 + r] + srow[5 * 64 + r];
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
-                dbp[r * H] = from_f32<TO>(dbeta * P.beta[i] * (1.f - P.beta[i]));
+                dbp[r * H] = from_f32<TO>(dbeta * P.dsig[i]);
             }
         }
     }
@@ -1741,7 +1742,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParam
     const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
 
     // ---------------- prep (rows r_i = 16w+4qg+i, key cols CPL*cl+e) ----------------
-    float qh[4][CPL], kh[4][CPL], G[4][CPL], vv[4][VPL], dov[4][VPL], beta[4], nq[4], nk[4];
+    float qh[4][CPL], kh[4][CPL], G[4][CPL], vv[4][VPL], dov[4][VPL], beta[4], dsig[4], nq[4], nk[4];
     float GC[CPL];
     {
         float rg[4][CPL], rb[4];
@@ -1769,6 +1770,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParam
                 nk[i] = 1.f;
             }
             beta[i] = (r < L) ? 1.f / (1.f + fast_exp(-rb[i])) : 0.f;
+            dsig[i] = (r < L) ? sigmoid_deriv(rb[i]) : 0.f;
             const float iq = p.scale / nq[i], ik = 1.f / nk[i];
 #pragma unroll
             for (int e = 0; e < CPL; ++e) { qh[i][e] *= iq; kh[i][e] *= ik; }
@@ -2226,7 +2228,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParam
             }
             if (cl == 0) {
                 const float dbeta = db + sm.dbv[0][r] + sm.dbv[1][r] + sm.dbv[2][r] + sm.dbv[3][r];
-                dbp[tok * H + h] = from_f32<TO>(dbeta * beta[i] * (1.f - beta[i]));
+                dbp[tok * H + h] = from_f32<TO>(dbeta * dsig[i]);
             }
         }
     }

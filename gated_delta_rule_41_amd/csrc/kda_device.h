@@ -210,6 +210,13 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// sigma'(b) = sigma(b) sigma(-b) = e / (1 + e)^2 with e = exp(-|b|): no 1 - sigma(b)
+// cancellation for large logits, and no overflow for very negative ones
+__device__ __forceinline__ float sigmoid_deriv(float b) {
+    const float e = fast_exp(-fabsf(b));
+    const float d = 1.f + e;
+    return e / (d * d);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 // (I + N)^{-1} for one strictly lower-triangular 16x16 block N (fp32), by the

@@ -114,9 +114,10 @@ size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32
 /* Forward.  o: [total_tokens, H, dv] in out_dtype.  initial_state: fp32
  * [num_seqs, H, dk, dv] or NULL (zero state; every document starts from its
  * own entry, never from the previous document).  final_state: fp32
- * [num_seqs, H, dk, dv] or NULL.  saved: required (kda_saved_size bytes) iff
- * flags has KDA_FLAG_SAVE_FOR_BWD, else ignored.  workspace may be NULL when
- * kda_fwd_workspace_size() is 0.
+ * [num_seqs, H, dk, dv] or NULL.  saved: required iff flags has
+ * KDA_FLAG_SAVE_FOR_BWD, else ignored; saved_bytes is its size, and a
+ * buffer smaller than kda_saved_size() returns KDA_ERR_WORKSPACE.  workspace
+ * may be NULL when kda_fwd_workspace_size() is 0.
  *
  * Long sequences.  With bf16 inputs, no KDA_FLAG_SAVE_FOR_BWD and no
  * KDA_FLAG_SEQUENTIAL, when there are few (sequence, head) chains for the
@@ -132,12 +133,13 @@ size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32
 kda_status kda_fwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
                    const void* k, const void* v, const void* g, const void* beta,
                    const int32_t* cu_seqlens, const float* initial_state, void* o,
-                   float* final_state, void* saved, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   float* final_state, void* saved, size_t saved_bytes, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Backward of kda_fwd for the loss <dO, o> + <dS_final, final_state>.
  * Takes the same inputs as the forward plus `saved` (filled by a forward with
- * KDA_FLAG_SAVE_FOR_BWD on the same inputs), dO ([total_tokens, H, dv],
+ * KDA_FLAG_SAVE_FOR_BWD on the same inputs; saved_bytes is its size, checked
+ * against kda_saved_size() as in kda_fwd), dO ([total_tokens, H, dv],
  * in_dtype) and dS_final (fp32 [num_seqs, H, dk, dv] or NULL = 0).
  * Outputs, all in out_dtype: dq, dk, dg [total_tokens, H, dk] (gradients with
  * respect to the RAW q and k, through the L2 norm, and to g, the log-decay);
@@ -147,7 +149,7 @@ kda_status kda_fwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs
 kda_status kda_bwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
                    const void* k, const void* v, const void* g, const void* beta,
                    const int32_t* cu_seqlens, const float* initial_state, const void* saved,
-                   const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                   size_t saved_bytes, const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
                    void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                    void* stream);
 
@@ -165,13 +167,13 @@ kda_status kda_bwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs
 kda_status kda_bwd_scan(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
                         const void* k, const void* v, const void* g, const void* beta,
                         const int32_t* cu_seqlens, const float* initial_state, const void* saved,
-                        const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                        size_t saved_bytes, const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
                         void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                         void* stream);
 kda_status kda_bwd_grads(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
                          const void* k, const void* v, const void* g, const void* beta,
                          const int32_t* cu_seqlens, const float* initial_state, const void* saved,
-                         const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
+                         size_t saved_bytes, const void* dO, const float* dS_final, void* dq, void* dk, void* dv, void* dg,
                          void* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                          void* stream);
 

@@ -52,8 +52,8 @@ def test_sizes():
     assert _lib.kda_saved_size(bad, 256, 1) == 0
 
 
-def _fwd(cfg, T=128, N=1, q=FAKE, o=FAKE, cu=0, saved=0, ws=0, wsb=0):
-    return _lib.kda_fwd_raw(cfg, T, N, q, FAKE, FAKE, FAKE, FAKE, cu, 0, o, 0, saved, ws, wsb, 0)
+def _fwd(cfg, T=128, N=1, q=FAKE, o=FAKE, cu=0, saved=0, saved_bytes=0, ws=0, wsb=0):
+    return _lib.kda_fwd_raw(cfg, T, N, q, FAKE, FAKE, FAKE, FAKE, cu, 0, o, 0, saved, saved_bytes, ws, wsb, 0)
 
 
 def _err():
@@ -76,7 +76,7 @@ def test_fwd_rejects_unsupported_configs(dk, dv, chunk, ind, expect):
 
 def test_fwd_rejects_bad_arguments():
     cfg = _lib.make_config(2, 64, 64, KDA_BF16)
-    assert _lib.load().kda_fwd(None, 1, 1, *([None] * 11), 0, None) == KDA_ERR_INVALID_ARG
+    assert _lib.load().kda_fwd(None, 1, 1, *([None] * 10), 0, None, 0, None) == KDA_ERR_INVALID_ARG
     assert _fwd(cfg, T=-1) == KDA_ERR_INVALID_ARG
     assert _fwd(cfg, T=1 << 31) == KDA_ERR_INVALID_ARG
     assert _fwd(cfg, N=0) == KDA_ERR_INVALID_ARG
@@ -87,6 +87,9 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(cfg, cu=FAKE + 4) == KDA_ERR_INVALID_ARG
     cfg.flags = KDA_FLAG_SAVE_FOR_BWD
     assert _fwd(cfg) == KDA_ERR_INVALID_ARG and "saved" in _err()
+    need = _lib.kda_saved_size(cfg, 128, 1)
+    assert need > 0
+    assert _fwd(cfg, saved=FAKE, saved_bytes=need - 1) == KDA_ERR_WORKSPACE and "saved" in _err()
     cfg.flags = 1 << 5
     assert _fwd(cfg) == KDA_ERR_INVALID_ARG
     cfg.flags = 0
@@ -105,13 +108,20 @@ def test_bwd_rejects_bad_arguments():
     need = _lib.kda_bwd_workspace_size(cfg, T, N)
     assert need > 0
 
-    def call(wsb=need, **kw):
+    saved_need = _lib.kda_saved_size(cfg, T, N)
+    assert saved_need > 0
+
+    def call(wsb=need, saved_bytes=saved_need, **kw):
         a = dict(args)
         a.update(kw)
         return _lib.kda_bwd_raw(cfg, T, N, a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["s0"], a["saved"],
-                                a["dO"], a["dSf"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dS0"], a["ws"], wsb, 0)
+                                saved_bytes, a["dO"], a["dSf"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dS0"], a["ws"], wsb, 0)
 
     assert call(wsb=need - 1) == KDA_ERR_WORKSPACE
+    assert call(saved_bytes=saved_need - 1) == KDA_ERR_WORKSPACE and "saved" in _err()
+    for stage in ("scan", "grads"):
+        assert _lib.kda_bwd_raw(cfg, T, N, *([FAKE] * 5), 0, 0, FAKE, saved_need - 256, FAKE, 0, *([FAKE] * 5), 0,
+                                FAKE, need, 0, stage=stage) == KDA_ERR_WORKSPACE
     assert call(saved=0) == KDA_ERR_INVALID_ARG and "saved" in _err()
     assert call(dO=0) == KDA_ERR_INVALID_ARG and "dO" in _err()
     assert call(dg=FAKE + 8) == KDA_ERR_INVALID_ARG

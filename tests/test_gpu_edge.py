@@ -81,19 +81,13 @@ def test_degenerate_heads_forward_backward(dtype, dk, dv):
     states = ("sf", "dS0")
     for name, a in got.items():
         assert np.isfinite(a).all(), (dtype, name)
-    # beta'(+-30) is ~1e-13, so head 2's dbeta is measured against the scale of the other
-    # heads' dbeta (fp32 rounds sigmoid(30) to 1, so the kernel's beta (1 - beta) is 0 there:
-    # an absolute error of ~1e-13, not a relative one)
-    db_scale = want["db"][:, [0, 1, 3]]
+    # head 2's dbeta carries sigma'(+-30) ~ 1e-13 and is measured on its own scale: the
+    # kernels form sigma'(b) as exp(-|b|) / (1 + exp(-|b|))^2, with no 1 - sigma(b) cancellation
     for h in range(4):
         errs = {}
         for name, a in got.items():
             ah, rh = a[:, h], want[name][:, h]
-            if name == "db" and h == 2:
-                errs[name] = _err(ah, rh, dtype) * (_scale(rh, dtype) / _scale(db_scale, dtype))
-            else:
-                errs[name] = _err(ah, rh, dtype, state=name in states)
+            errs[name] = _err(ah, rh, dtype, state=name in states)
         _say(f"head {h}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
         for name, e in errs.items():
             assert e <= _bar(dtype, state=name in states), (dtype, h, name, e)
-    assert np.abs(got["db"][:, 2]).max() <= 1e-9 * _scale(db_scale, "bf16")
