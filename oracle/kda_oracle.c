@@ -237,7 +237,7 @@ int kda_oracle_fwd_core(int64_t T, int N, const int64_t* cu, int H, int dk, int 
  *     dalpha_t[i] = sum_j R'[i,j] S_{t-1}[i,j] ;  dg_t = alpha_t * dalpha_t
  *     R = Diag(alpha_t) R'
  * then through the normalisation and the sigmoid (the saved norms are reused):
- *     dq = (dqh - qh (qh . dqh)) / n_q,  dk likewise,  db = dbeta beta (1 - beta)
+ *     dq = (dqh - qh (qh . dqh)) / n_q,  dk likewise,  db = dbeta sigma(b) sigma(-b)
  * d(initial state) = R after the first token.  States are checkpointed every
  * SEG tokens and each segment is recomputed during the reverse sweep. */
 #define SEG 64
@@ -364,7 +364,14 @@ static void* bwd_worker(void* arg) {
                         dkr[i] = (dkh[i] - kh[i] * ak) / nk;
                     }
                 }
-                J->db[t * H + h] = J->prepared ? dbeta : dbeta * beta * (1.0 - beta);
+                if (J->prepared) {
+                    J->db[t * H + h] = dbeta;
+                } else {
+                    /* sigma'(b) = sigma(b) sigma(-b) = e / (1 + e)^2, e = exp(-|b|): the
+                     * form beta (1 - beta) keeps only ~3 digits of 1 - beta at |b| = 30 */
+                    const double e = exp(-fabs(J->b[t * H + h]));
+                    J->db[t * H + h] = dbeta * (e / ((1.0 + e) * (1.0 + e)));
+                }
                 (void)tmpk;
             }
         }

@@ -252,6 +252,23 @@ def test_backward_matches_central_differences(lens):
         assert err < 1e-7, (name, err)
 
 
+@pytest.mark.parametrize("logit", [-40.0, -30.0, 0.5, 30.0, 40.0])
+def test_single_token_beta_gradient_closed_form(logit):
+    """One token from the zero state: S_1 = beta kh v^T and o = beta (kh . qh) v,
+    so dL/db = sigma'(b) (kh . qh) (v . dO) for L = <dO, o>.  sigma'(b) is taken
+    as 1 / (2 + 2 cosh b), which has no cancellation at large |b|, so the pin
+    holds to fp64 rounding even where 1 - sigma(b) is below 1e-13."""
+    rng = np.random.default_rng(11)
+    dk, dv = 8, 6
+    q, k, v, g, _ = _rand_case(rng, 1, 1, dk, dv)
+    b = np.full((1, 1), logit)
+    dO = rng.normal(size=(1, 1, dv))
+    qh, kh, _, _ = _prep(q, k, g, b)
+    want = (kh[0, 0] @ qh[0, 0]) * (v[0, 0] @ dO[0, 0]) / (2.0 + 2.0 * np.cosh(logit))
+    got = oracle.bwd(q, k, v, g, b, dO)["db"][0, 0]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+
+
 def test_core_backward_matches_central_differences():
     """Gradients with respect to prepared inputs (alpha, beta directly)."""
     rng = np.random.default_rng(14)
