@@ -59,6 +59,14 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    # One HIP runtime per process.  PyTorch ships its own libamdhip64 and
+    # libhsa-runtime64; loading torch first makes libkda.so bind to those (same
+    # soname) instead of pulling in a second copy from the ROCm install, and two
+    # runtimes in one process compete for the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     cfgp = ctypes.POINTER(KdaConfig)
     lib.kda_config_init.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
