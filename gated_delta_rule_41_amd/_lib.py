@@ -78,6 +78,8 @@ def load():
     lib.kda_fwd.argtypes = ([cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
                             + [ctypes.c_size_t, _vp])
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_static.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
+    lib.kda_fwd_static.restype = ctypes.c_int
     for name in ("kda_bwd", "kda_bwd_scan", "kda_bwd_grads"):
         fn = getattr(lib, name)
         fn.argtypes = ([cfgp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 8 + [ctypes.c_size_t] + [_vp] * 9
@@ -126,6 +128,17 @@ def kda_fwd_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initi
     """Direct call of kda_fwd with integer device addresses (0 = NULL); returns the status."""
     return load().kda_fwd(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens,
                           initial_state, o, final_state, saved, saved_bytes, workspace, workspace_bytes, stream)
+
+
+KDA_STATIC_WORKSPACE_BYTES = 128 << 20
+
+
+def kda_fwd_static_raw(cfg, total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens, initial_state, o,
+                       final_state, saved, saved_bytes, stream) -> int:
+    """Direct call of kda_fwd_static (the forward on the library's static
+    workspace) with integer device addresses (0 = NULL); returns the status."""
+    return load().kda_fwd_static(ctypes.byref(cfg), total_tokens, num_seqs, q, k, v, g, beta, cu_seqlens,
+                                 initial_state, o, final_state, saved, saved_bytes, stream)
 
 
 BWD_ENTRY = {"all": "kda_bwd", "scan": "kda_bwd_scan", "grads": "kda_bwd_grads"}

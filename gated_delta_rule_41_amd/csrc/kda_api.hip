@@ -2,11 +2,14 @@
 //
 // Validates every argument on the host before any HIP call, sizes the saved
 // and workspace buffers, and hands the work to the kernel launchers.  The
-// library allocates nothing and keeps no global state apart from the
-// thread-local error text.
+// library allocates nothing.  Its only global state is the thread-local error
+// text and, for kda_fwd_static, one static device workspace per GPU with the
+// table of its device addresses.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_internal.h"
@@ -242,6 +245,39 @@ kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q
     return KDA_OK;
 }
 
+// ---------------------------------------------------------- static workspace
+// kda_fwd_static's workspace: one array per GPU, placed by the code object
+// loader, held until the process ends.  Host code never passes `scratch`
+// itself (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[KDA_STATIC_WORKSPACE_BYTES];
+// the host check of a call's workspace against the array uses the array's own size
+constexpr size_t kStaticWorkspaceBytes = sizeof(scratch);
+static_assert(kStaticWorkspaceBytes == KDA_STATIC_WORKSPACE_BYTES, "static workspace size");
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+kda_status static_workspace(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_UNSUPPORTED, "device index out of range%s");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetSymbolAddress of the static workspace failed: %s",
+                                         hipGetErrorString(e));
+        if (!ptr) return fail(KDA_ERR_HIP, "the static workspace has no device address%s");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return KDA_OK;
+}
+
 }  // namespace
 
 #define KDA_TRY(x) KDA_TRY_(x)
@@ -288,6 +324,24 @@ kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, c
     if (workspace_bytes < ws_need) return fail(KDA_ERR_WORKSPACE, "workspace too small%s");
     if (ws_need > 0) KDA_TRY(need_ptr(workspace, "workspace"));
     return fwd_launch(cfg, T, N, q, k, v, g, beta, cu, s0, o, sfinal, saved, workspace, (hipStream_t)stream);
+}
+
+kda_status kda_fwd_static(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
+                          const void* v, const void* g, const void* beta, const int32_t* cu,
+                          const float* s0, void* o, float* sfinal, void* saved, size_t saved_bytes,
+                          void* stream) {
+    g_err[0] = 0;
+    KDA_TRY(fwd_check(cfg, T, N, q, k, v, g, beta, cu, s0, o, sfinal, saved, saved_bytes));
+    const size_t ws_need = kda_fwd_workspace_size(cfg, T, N);
+    if (ws_need > kStaticWorkspaceBytes) {
+        snprintf(g_err, sizeof g_err,
+                 "the call needs %zu bytes of workspace, above the static workspace's %zu: call kda_fwd",
+                 ws_need, kStaticWorkspaceBytes);
+        return KDA_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if (ws_need > 0) KDA_TRY(static_workspace(&ws));
+    return fwd_launch(cfg, T, N, q, k, v, g, beta, cu, s0, o, sfinal, saved, ws, (hipStream_t)stream);
 }
 
 kda_status kda_decode(const kda_config* cfg, int32_t N, const void* q, const void* k, const void* v,

@@ -35,9 +35,10 @@
  *  - All pointers except the config are device pointers (hipMalloc'ed or
  *    equivalent), 16-byte aligned, and owned by the caller.  Inputs are read
  *    only; outputs are fully overwritten.  The library never allocates, frees,
- *    synchronises or changes the current device, and keeps no global state:
- *    every entry point is re-entrant.  All work is enqueued on `stream` (a
- *    hipStream_t passed as void*; NULL is the null stream).
+ *    synchronises or changes the current device, and keeps no global state
+ *    apart from kda_fwd_static's workspace: every other entry point is
+ *    re-entrant.  All work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the null stream).
  *  - Errors.  Arguments are validated on the host BEFORE any HIP call; a bad
  *    argument returns KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED /
  *    KDA_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
@@ -135,6 +136,25 @@ kda_status kda_fwd(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs
                    const int32_t* cu_seqlens, const float* initial_state, void* o,
                    float* final_state, void* saved, size_t saved_bytes, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* kda_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, checks and results are those of kda_fwd;
+ * when the call needs a workspace (the long-sequence split), it uses a static
+ * device array of KDA_STATIC_WORKSPACE_BYTES that the library holds on every
+ * GPU it runs on until the process ends (one copy per GPU, found once per
+ * device on its first use here).  A call whose kda_fwd_workspace_size()
+ * exceeds that returns KDA_ERR_WORKSPACE and enqueues nothing.  Every call on
+ * one GPU shares that GPU's array: calls on one GPU that can overlap (other
+ * host threads, or work on other streams still in flight) race and must be
+ * ordered by the caller.  The array needs no clearing: every byte a call reads
+ * is written by that call first.  No hipMalloc, hipFree or other allocating
+ * call is made. */
+#define KDA_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+kda_status kda_fwd_static(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, const void* q,
+                          const void* k, const void* v, const void* g, const void* beta,
+                          const int32_t* cu_seqlens, const float* initial_state, void* o,
+                          float* final_state, void* saved, size_t saved_bytes, void* stream);
 
 /* Backward of kda_fwd for the loss <dO, o> + <dS_final, final_state>.
  * Takes the same inputs as the forward plus `saved` (filled by a forward with
