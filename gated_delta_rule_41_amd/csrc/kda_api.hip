@@ -55,12 +55,7 @@ kda_status check_config_common(const kda_config* c) {
 }
 
 // Config check shared by the chunked entry points.
-kda_status check_config(const kda_config* c) {
-    KDA_TRY_(check_config_common(c));
-    if (c->in_dtype == KDA_F32 && c->dk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "fp32 inputs support dk = 64 only%s");
-    return KDA_OK;
-}
+kda_status check_config(const kda_config* c) { return check_config_common(c); }
 
 // One launch covers at most 2^32 - 1 work-items along x (the dispatch packet's
 // grid size is a 32-bit count of work-items).
@@ -158,9 +153,13 @@ SplitPlan split_plan(const kda_config* c, int64_t T, int32_t N) {
     return s;
 }
 
-// dL/dS at the end of every chunk (state type), then dU of every chunk.
+// dL/dS at the end of every chunk (state type), then dU of every chunk, then
+// one flag per chunk and head (decay past the factorised kernels' range).
 size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
     return align256((size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c));
+}
+size_t bwd_flag_bytes(const kda_config* c, int64_t T, int32_t N) {
+    return align256((size_t)kda::num_slots(T, N) * c->H * sizeof(int32_t));
 }
 
 // Every argument check of kda_fwd except the workspace's.
@@ -310,7 +309,7 @@ size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
 
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
     if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
-    return bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N));
+    return bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)) + bwd_flag_bytes(cfg, T, N);
 }
 
 kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
@@ -426,6 +425,7 @@ static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t
         p.u_saved = (const float*)(base + L.u);
         p.du_ws = (float*)((char*)workspace + bwd_dst_bytes(cfg, T, N));
     }
+    p.chunk_flags = (int32_t*)((char*)workspace + bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)));
     p.dq = dq; p.dk = dk; p.dv_out = dv; p.dg = dg; p.db = dbeta; p.dS0 = dS0;
     p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
     p.seqlen = cu ? 0 : (int32_t)(T / N);

@@ -27,6 +27,7 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_token.h"
 
 namespace kda {
 
@@ -55,6 +56,7 @@ struct __attribute__((aligned(32))) ScanSmem {
     float tdiag[4][16][20];
     float gc[DK];
     float red[4][DK];
+    int token_path;            // the chunk's decay passes kTokenBelow: step it token by token
 };
 
 template <typename T, int DK>
@@ -183,6 +185,30 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_scan_kernel(BwdParams p) 
         if (w == 0 && qg == 0) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = fast_exp(GC[e]);
+        }
+        {
+            // decay past the factorised range: the transposed recurrence token by
+            // token (every wave holds every channel's sum, so the branch is uniform)
+            bool tok = false, exact = false;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                tok |= !(GC[e] >= kTokenBelow);
+                exact |= !(GC[e] >= kExactBelow);
+            }
+            const bool xexact = __builtin_amdgcn_ballot_w64(exact) != 0;
+            if (slice == 0 && tid == 0) p.chunk_flags[slot * H + h] = xexact ? 1 : 0;
+            if (__builtin_amdgcn_ballot_w64(tok) != 0) {
+                if (jc > 0) load_chunk(c0 - kChunk);
+                float* out = dst + (slot * H + h) * (int64_t)DK * dv;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) out[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
+                const TokSrc<T> src = {qp, kp, gp, bp, dop, H, h, dv, vcol, qg, p.eps, p.scale};
+                token_bwd<T, DK>(dS, src, c0, L);
+                __syncthreads();
+                continue;
+            }
         }
         float qgv[CPL][4], ktv[CPL][4];
 #pragma unroll
@@ -450,6 +476,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     V4T xqh[4][CQ], xql[4][CQ];   // qh Gam hi/lo of the chunk to run next
     RawRow<T, VPL> xdo[4];        // its dO slice
     float xgc[CPL];               // its Gam_C
+    bool xtok = false;            // its decay passes kTokenBelow
+    bool xexact = false;          // its decay passes kExactBelow
 
     // part: -1 all rows; 0 q and beta; 1 k; 2 g and dO.  The second buffer is
     // filled in parts over three steps: a wave stalls at issue while its
@@ -528,6 +556,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
     // (hi, lo) are written now.
     auto prep_b = [&]() {
         float goff[CPL];
+        bool tok = false, exact = false;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
             const int c = CPL * cl + e;
@@ -540,7 +569,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
             }
             goff[e] = a;
             xgc[e] = fast_exp2(tot * kLog2e);
+            tok |= !(tot >= kTokenBelow);
+            exact |= !(tot >= kExactBelow);
         }
+        xtok = __builtin_amdgcn_ballot_w64(tok) != 0;
+        xexact = __builtin_amdgcn_ballot_w64(exact) != 0;
 #pragma unroll
         for (int e4 = 0; e4 < CQ; ++e4) {
             f32x4 G[4];
@@ -674,6 +707,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
                     for (int i = 0; i < 4; ++i) *atb(out, ob + (unsigned)((16 * mb + i) * dv) * 4u) = dS[mb][i];
             }
             lds_barrier();
+            if (__builtin_amdgcn_readfirstlane(sm.token_path)) {
+                // decay past the factorised range: the transposed recurrence token
+                // by token (no dU for this chunk: the pair-exact gradient kernel
+                // recomputes it); the prep waves' barriers are met with no work
+                refresh();
+                const int64_t c0 = t0 + jc * kChunk;
+                const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+                const TokSrc<T> src = {qp, kp, gp, bp, dop, H, h, dv, vcol, qg, p.eps, p.scale};
+                token_bwd<T, DK>(dS, src, c0, L);
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
+                continue;
+            }
             refresh();
             intra_products();
             lds_barrier();
@@ -793,6 +842,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdP
 #pragma unroll
                     for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
                 }
+                if (ww == 0 && l == 0) {
+                    sm.token_path = xtok ? 1 : 0;
+                    if (slice == 0) p.chunk_flags[(t0 / kChunk + n + jc) * H + h] = xexact ? 1 : 0;
+                }
             }
             lds_barrier();
             refresh();
@@ -852,17 +905,6 @@ __device__ __forceinline__ void st_blk(float* M, int ld, int m0, int n0, f32x4 x
     for (int i = 0; i < 4; ++i) M[(m0 + 4 * qg + i) * ld + n0 + cl] = x[i];
 }
 
-// Find the sequence that owns state slot `slot` (slot = floor(cu[n]/64) + n + j).
-__device__ __forceinline__ int slot_owner(const int32_t* cu, int N, int seqlen, int64_t slot) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        const int64_t start = cu ? (int64_t)cu[mid] : (int64_t)mid * seqlen;
-        if (start / kChunk + mid <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
 
 // Slot layout of the chunk kernel's LDS (bytes).
 template <typename T, int DK, int DV>
@@ -1044,7 +1086,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // g, which the first call leaves in LDS.
     struct Prep {
         RawRow<T, CPH> q[4], k[4];
-        float G[4][CPH], GC[CPH], beta[4], dsig[4], iq[4], ik[4];
+        float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4];
     };
     // after_loads runs once the row loads are issued, before their first use:
     // more loads issued there wait only behind these
@@ -1070,7 +1112,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             P.q[i].keep(ok); P.k[i].keep(ok); rg[i].keep(ok);
             // v_rcp (~1 ulp), as the forward forms beta and the reciprocal norms
             P.beta[i] = ok ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
-            P.dsig[i] = ok ? sigmoid_deriv(rb[i]) : 0.f;
             P.iq[i] = p.scale * __builtin_amdgcn_rcpf(ok ? nq[i] : 1.f);
             P.ik[i] = __builtin_amdgcn_rcpf(ok ? nk[i] : 1.f);
         }
@@ -1638,7 +1679,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             if (wh == 0 && cl == 0) {
                 const float db = srow[2 * 64 + r] + srow[5 * 64 + r];
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
-                dbp[r * H] = from_f32<TO>(dbeta * P.dsig[i]);
+                // sigma'(b) from the logit itself (reloaded: one value per row)
+                dbp[r * H] = from_f32<TO>(dbeta * sigmoid_deriv(gload1(bc + r * H)));
             }
         }
     }
@@ -2269,7 +2311,13 @@ static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t s) {
         const hipError_t e = launch_scan<T, DK>(p, s);
         if (e != hipSuccess) return e;
     }
-    if (stages & kBwdGrads) return launch_chunk<T, TO, DK>(p, s);
+    if (stages & kBwdGrads) {
+        const hipError_t e = launch_chunk<T, TO, DK>(p, s);
+        if (e != hipSuccess) return e;
+        // chunks past the factorised range are recomputed pair by pair (kda_exact.hip)
+        return launch_bwd_exact(p, std::is_same<T, bf16>::value ? 1 : 0, std::is_same<TO, bf16>::value ? 1 : 0, DK,
+                                true, s);
+    }
     return hipSuccess;
 }
 
@@ -2279,6 +2327,15 @@ hipError_t launch_bwd(const BwdParams& p, int in_dtype, int out_dtype, int dk, i
             return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 128>(p, stages, s)
                                   : launch_bwd_t<bf16, float, 128>(p, stages, s);
         return out_dtype == 1 ? launch_bwd_t<bf16, bf16, 64>(p, stages, s) : launch_bwd_t<bf16, float, 64>(p, stages, s);
+    }
+    if (dk == 128) {
+        // fp32 inputs at dk = 128: token-by-token reverse scan, pair-exact chunk gradients
+        if (stages & kBwdScan) {
+            const hipError_t e = launch_bwd_scan_token(p, in_dtype, dk, s);
+            if (e != hipSuccess) return e;
+        }
+        if (stages & kBwdGrads) return launch_bwd_exact(p, in_dtype, out_dtype, dk, false, s);
+        return hipSuccess;
     }
     return out_dtype == 1 ? launch_bwd_t<float, bf16, 64>(p, stages, s) : launch_bwd_t<float, float, 64>(p, stages, s);
 }

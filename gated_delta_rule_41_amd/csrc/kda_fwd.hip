@@ -35,6 +35,7 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_token.h"
 
 namespace kda {
 
@@ -228,6 +229,27 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
                     p.nq_saved[(c0 + r) * H + h] = nq[i];
                     p.nk_saved[(c0 + r) * H + h] = nk[i];
                 }
+            }
+        }
+        {
+            // decay past the factorised range: the recurrence token by token
+            // (every wave holds every channel's sum, so the branch is uniform)
+            bool tok = false;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) tok |= !(GC[e] >= kTokenBelow * kLog2e);
+            if (__builtin_amdgcn_ballot_w64(tok) != 0) {
+                if (c0 + kChunk < t1) load_chunk(c0 + kChunk);
+                if (SAVE) {
+                    float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = S[mb][i];
+                }
+                const TokSrc<T> src = {qp, kp, gp, bp, vp, H, h, dv, vcol, qg, p.eps, p.scale};
+                token_fwd<T, TO, DK>(S, src, c0, L, op, nullptr, nullptr, false);
+                __syncthreads();
+                continue;
             }
         }
         // operand tiles: qh Gam, beta kh Gam, kh / Gam
@@ -470,7 +492,9 @@ hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t s) { return l
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save,
                       hipStream_t s) {
     if (in_dtype == 1) return launch_fwd16(p, out_dtype, dk, save, s);
-    // fp32 inputs: fp32 MFMA; dk = 64 only (the fp32 tiles of dk = 128 exceed LDS)
+    // fp32 inputs: fp32 MFMA at dk = 64; at dk = 128 (whose fp32 tiles exceed
+    // LDS) the recurrence token by token (kda_exact.hip)
+    if (dk == 128) return launch_fwd_token(p, in_dtype, out_dtype, dk, save, s);
     return out_dtype == 1 ? launch_fwd_t<float, bf16, 64>(p, save, s)
                           : launch_fwd_t<float, float, 64>(p, save, s);
 }

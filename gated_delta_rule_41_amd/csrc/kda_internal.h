@@ -38,6 +38,18 @@ struct KtFrag {
 // The map is collision-free and bounded by floor(T/64) + N (see kda_api.hip).
 inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }
 
+// The sequence that owns state slot `slot` (the inverse of the map above).
+__device__ __forceinline__ int slot_owner(const int32_t* cu, int N, int seqlen, int64_t slot) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int64_t start = cu ? (int64_t)cu[mid] : (int64_t)mid * seqlen;
+        if (start / kChunk + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -92,6 +104,8 @@ struct BwdParams {
     void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
     const float* u_saved;    // forward's U of every chunk [slots,H,dv,64] (bf16 inputs)
     float* du_ws;            // workspace: dU of every chunk [slots,H,dv,64] (bf16 inputs)
+    int32_t* chunk_flags;    // workspace [slots,H]: 1 where the chunk's decay passes the factorised
+                             // range (written by the reverse scan, read by the pair-exact kernel)
     void* dq;
     void* dk;
     void* dv_out;
@@ -132,5 +146,13 @@ hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t stream);
 hipError_t launch_fwd16(const FwdParams& p, int out_dtype, int dk, bool save, hipStream_t stream);
 hipError_t launch_fwd16_maps(const FwdParams& p, int dk, hipStream_t stream);
 hipError_t launch_carry(const CarryParams& p, int dk, hipStream_t stream);
+// Kernels without the chunk-start gate factorisation (kda_exact.hip): the
+// forward and the reverse scan token by token, and the chunk gradients with
+// the decay of every token pair formed directly (only_unsafe: only chunks whose
+// decay passes the factorised kernels' range; the others are left as they are).
+hipError_t launch_fwd_token(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save, hipStream_t stream);
+hipError_t launch_bwd_scan_token(const BwdParams& p, int in_dtype, int dk, hipStream_t stream);
+hipError_t launch_bwd_exact(const BwdParams& p, int in_dtype, int out_dtype, int dk, bool only_unsafe,
+                            hipStream_t stream);
 
 }  // namespace kda

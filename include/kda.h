@@ -50,16 +50,20 @@
  *    undefined behaviour; the kernels clamp every document to
  *    [0, total_tokens) so it cannot address memory outside the buffers.
  *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
- *    {KDA_F32, KDA_BF16}, with fp32 inputs only at dk = 64 in kda_fwd and
- *    kda_bwd (kda_decode takes both dk); H >= 1 with
- *    64 * H * max(dk, dv) < 2^31 (the kernels address a chunk's rows with
- *    32-bit offsets); total_tokens < 2^31; one launch covers at most
- *    2^32 - 1 work-items, so num_seqs * H * dv/64 and
- *    (total_tokens/64 + num_seqs) * H stay below 2^23 (kda_decode:
+ *    {KDA_F32, KDA_BF16}; H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
+ *    kernels address a chunk's rows with 32-bit offsets); total_tokens < 2^31;
+ *    one launch covers at most 2^32 - 1 work-items, so num_seqs * H * dv/64
+ *    and (total_tokens/64 + num_seqs) * H stay below 2^23 (kda_decode:
  *    num_seqs * H * dv/64 below 2^24).  Outside these, KDA_ERR_UNSUPPORTED.
- *    Per-chunk cumulative log-decay sum_{chunk} g >= -80 per channel (the
- *    kernels factor exp(G_r - G_s) = exp(G_r) exp(-G_s) inside a 64-token
- *    chunk).
+ *  - Gates: any g <= 0 (decay alpha in (0, 1]).  The matrix-core kernels
+ *    factor the decay between two tokens of a chunk against a reference
+ *    point; a chunk in which some channel decays past that factorisation's
+ *    fp32 range (a per-chunk sum of g below about -60 per channel, or a
+ *    16-token block below about -9.7 in the bf16 forward) runs through the
+ *    recurrence token by token in the forward and the reverse scan, and its
+ *    gradients through a kernel that forms the decay of every token pair
+ *    directly.  The result is the same up to rounding; such chunks are slower.
+ *    fp32 inputs at dk = 128 take those kernels for every chunk.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -14,7 +14,10 @@ round-to-nearest-even to float32 and, for bf16 runs, to bfloat16):
 * g (log-decay) = -softplus(x), x ~ N(-2, 1), so alpha = exp(g) lies in (0, 1);
 * initial state S0 and dS_final ~ N(0, 0.01) (standard deviation 0.1), fp32;
 * packed documents: lengths ~ lognormal(6.5, 1), rescaled to the total token
-  count (floored, at least 1, remainder to the largest fractional parts).
+  count (floored, at least 1, remainder to the largest fractional parts);
+* gate-range mix (``mix_gates``): per head, one channel in three keeps the
+  draw above, one in three has g = 0 (no decay) and one in three fast-forgetting
+  g ~ U(-8, -2) per token (a 64-token chunk then decays by e^-128 .. e^-512).
 
 Arrays are returned as float32 whose values are exactly representable in the
 run dtype; the oracle upcasts them exactly to float64.
@@ -27,7 +30,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 BLOCK = 1 << 16
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "b": 3, "g": 4, "s0": 5, "dO": 6, "dS": 7, "doclen": 8}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "b": 3, "g": 4, "s0": 5, "dO": 6, "dS": 7, "doclen": 8, "gmix": 9}
 
 # The five workloads: shapes, dtypes and which tensors exist.
 WORKLOADS = {
@@ -101,6 +104,20 @@ def _normal_tokens(seed, tid, T, tail_shape, dtype, mean=0.0, std=1.0, transform
         with ThreadPoolExecutor(max_workers=min(_workers(), nblk)) as ex:
             list(ex.map(one, range(nblk)))
     return out
+
+
+def mix_gates(g: np.ndarray, seed: int, dtype: str, offset: int = 0) -> np.ndarray:
+    """g [T, H, dk] with the gate-range mix applied per head: channel c with
+    (c + h + offset) % 3 == 0 keeps its value, == 1 is set to 0, == 2 is drawn
+    from U(-8, -2) (rounded to ``dtype``)."""
+    T, H, dk = g.shape
+    rng = np.random.default_rng([seed, TENSOR_IDS["gmix"], 0])
+    fast = round_to(rng.uniform(-8.0, -2.0, size=g.shape), dtype)
+    kind = (np.arange(dk)[None, :] + np.arange(H)[:, None] + offset) % 3   # [H, dk]
+    out = np.array(g, dtype=np.float32, copy=True)
+    out = np.where(kind[None] == 1, np.float32(0.0), out)
+    out = np.where(kind[None] == 2, fast, out)
+    return out.astype(np.float32)
 
 
 def doc_lengths(seed: int, ndocs: int, total: int) -> np.ndarray:

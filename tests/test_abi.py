@@ -44,10 +44,15 @@ def test_sizes():
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     u = slots * 32 * 64 * 128 * 4   # per-chunk U (saved) and dU (workspace), bf16 inputs only
     assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm) + al(u)
-    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states) + al(u)
+    flags = slots * 32 * 4          # one int per chunk and head: decay past the factorised range
+    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states) + al(u) + al(flags)
     assert _lib.kda_fwd_workspace_size(cfg, T, N) == 0
     cfg32 = _lib.make_config(2, 64, 64, KDA_F32, KDA_F32)
     assert _lib.kda_saved_size(cfg32, 256, 1) == al(5 * 2 * 64 * 64 * 4) + 2 * al(256 * 2 * 4)
+    # fp32 inputs at dk = 128: states and norms only (no per-chunk U)
+    cfg128 = _lib.make_config(2, 128, 128, KDA_F32, KDA_F32)
+    assert _lib.kda_saved_size(cfg128, 256, 1) == al(5 * 2 * 128 * 128 * 4) + 2 * al(256 * 2 * 4)
+    assert _lib.kda_bwd_workspace_size(cfg128, 256, 1) == al(5 * 2 * 128 * 128 * 4) + al(5 * 2 * 4)
     bad = _lib.make_config(2, 96, 64)
     assert _lib.kda_saved_size(bad, 256, 1) == 0
 
@@ -64,7 +69,6 @@ def _err():
     (96, 128, 64, KDA_BF16, KDA_ERR_UNSUPPORTED),
     (128, 32, 64, KDA_BF16, KDA_ERR_UNSUPPORTED),
     (128, 128, 32, KDA_BF16, KDA_ERR_UNSUPPORTED),
-    (128, 128, 64, KDA_F32, KDA_ERR_UNSUPPORTED),
     (128, 128, 64, 7, KDA_ERR_INVALID_ARG),
 ])
 def test_fwd_rejects_unsupported_configs(dk, dv, chunk, ind, expect):
