@@ -33,7 +33,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIB names another build of kda_oracle.c (the sanitizer test loads
+# an AddressSanitizer / UndefinedBehaviorSanitizer build this way)
+_LIB_PATH = os.environ.get("KDA_ORACLE_LIB") or os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
