@@ -102,7 +102,7 @@ FWD_GRID = 4 * 32 * 2 * 512   # threads in one launch of the workload's fused fo
 
 KERNELS = {   # traffic.json key -> (substring of the dispatched kernel name, source file, grid size or None)
     "grads": ("kda_bwd_grads_kernel<float, 128, 128>", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
-    "scan": ("kda_bwd_scan_bf16_kernel", "gated_delta_rule_41_amd/csrc/kda_bwd.hip", None),
+    "scan": ("kda_bwd_scan16_kernel", "gated_delta_rule_41_amd/csrc/kda_scan16.hip", None),
     "fwd": ("kda_fwd16_kernel<float, 128, true, false>", "gated_delta_rule_41_amd/csrc/kda_fwd16.hip", FWD_GRID),
     # the long-context run's second level launches the same kernel on another grid
     "fwd_infer": ("kda_fwd16_kernel<float, 128, false, false>", "gated_delta_rule_41_amd/csrc/kda_fwd16.hip",
@@ -405,7 +405,7 @@ def main():
 
     tokens = B * T
     names = {"fwd": "kda_fwd16_kernel (training forward, state save)",
-             "scan": "kda_bwd_scan_bf16_kernel (reverse state scan)",
+             "scan": "kda_bwd_scan16_kernel (reverse state scan)",
              "grads": "kda_bwd_grads_kernel (chunk-parallel gradients)"}
     dom = max(kms, key=kms.get)
     dbytes = alg_bytes(B, T, H, dk, dv, dom)

@@ -5,10 +5,11 @@
 // gradients ("TorchTitan Ascend open source: Kimi K3.1 Pro adaptation and
 // training practice", section "KDA pre/post-processing fusion").  Here:
 //
-//  B1  reverse state-gradient scan (kda_bwd_scan_bf16_kernel; kda_bwd_scan_kernel
-//      for fp32 inputs).  One persistent workgroup per (sequence, head,
-//      64-column value slice) walks the chunks backwards with dL/dS (dk x 64,
-//      fp32) resident in MFMA accumulators:
+//  B1  reverse state-gradient scan (kda_bwd_scan_kernel for fp32 inputs;
+//      kda_bwd_scan16_kernel in kda_scan16.hip for bf16 inputs).  One
+//      persistent workgroup per (sequence, head, 64-column value slice) walks
+//      the chunks backwards with dL/dS (dk x 64, fp32) resident in MFMA
+//      accumulators:
 //          dU  = Aqk^T dO + Ktil dS1
 //          dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
 //      and writes dS1 (dL/dS at the end of every chunk) and dU for B2.
@@ -56,7 +57,6 @@ struct __attribute__((aligned(32))) ScanSmem {
     float tdiag[4][16][20];
     float gc[DK];
     float red[4][DK];
-    int token_path;            // the chunk's decay passes kTokenBelow: step it token by token
 };
 
 template <typename T, int DK>
@@ -406,487 +406,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_scan_kernel(BwdParams p) 
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) p.dS0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
-    }
-}
-
-// ============================================================================
-// B1 for bf16 inputs: 8 waves in two groups of four, as in the forward.
-// The state waves own the dL/dS columns (diagonal inverses, dU and the dS
-// step); the prep waves prepare the previous chunk in registers while the
-// state waves run the step, and prefetch the one before it.
-// ============================================================================
-template <int DK>
-__global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan_bf16_kernel(BwdParams p) {
-    typedef bf16 T;
-    __shared__ ScanSmem<T, DK> sm;
-    typedef ScanSmem<T, DK> SM;
-    constexpr int PK = SM::PK;
-    constexpr int PC = SM::PC;
-    constexpr int CPL = DK / 16;
-    constexpr int CQ = CPL / 4;
-    constexpr int VPL = kSlice / 16;
-    constexpr int NKB = DK / 32;
-    constexpr int NMB = DK / 16;
-    typedef bf16x8 V8T;
-    typedef bf16x4 V4T;
-
-    const int tid = threadIdx.x, w = tid >> 6;
-    // Lane coordinates, re-derived at the top of every step from a lane index
-    // the optimiser cannot see through, so lane-dependent addresses and masks
-    // are recomputed per step instead of being held across the loop.
-    int l = tid & 63, qg = l >> 4, cl = l & 15;
-    const bool is_state = w < 4;
-    const int ww = w & 3;
-    int chain, slice;
-    map_block(blockIdx.x, p.N * p.H, p.nslices, chain, slice);
-    const int n = chain / p.H, h = chain % p.H;
-    int64_t t0, t1;
-    seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
-    const int dv = p.dv, H = p.H;
-    const int dv0 = slice * kSlice;
-    int vcol = dv0 + 16 * ww + cl;
-    auto refresh = [&]() {
-        asm volatile("" : "+v"(l));
-        qg = l >> 4;
-        cl = l & 15;
-        vcol = dv0 + 16 * ww + cl;
-    };
-    const int64_t nchunks = (t1 - t0 + kChunk - 1) / kChunk;
-
-    const T* __restrict__ qp = reinterpret_cast<const T*>(p.q);
-    const T* __restrict__ kp = reinterpret_cast<const T*>(p.k);
-    const T* __restrict__ gp = reinterpret_cast<const T*>(p.g);
-    const T* __restrict__ bp = reinterpret_cast<const T*>(p.b);
-    const T* __restrict__ dop = reinterpret_cast<const T*>(p.dO);
-    const int64_t rs_k = (int64_t)H * DK, rs_v = (int64_t)H * dv;
-
-    // ---------------- prep waves: rows 16ww+4qg+i, key columns CPL*cl+e
-    RawRow<T, CPL> rq[4], rk[4], rg[4];
-    RawRow<T, VPL> rdo[4];
-    RawScalar<T> rb[4];
-    float nq[4], nk[4], beta[4];
-    int Lp = 0;
-    // second buffer: the chunk after the one being prepared, loaded early in a
-    // step so that the address unit works under the LDS steps instead of
-    // stalling the end of the chunk
-    RawRow<T, CPL> nrq[4], nrk[4], nrg[4];
-    RawRow<T, VPL> nrdo[4];
-    RawScalar<T> nrb[4];
-    int nLp = 0;
-    V4T xqh[4][CQ], xql[4][CQ];   // qh Gam hi/lo of the chunk to run next
-    RawRow<T, VPL> xdo[4];        // its dO slice
-    float xgc[CPL];               // its Gam_C
-    bool xtok = false;            // its decay passes kTokenBelow
-    bool xexact = false;          // its decay passes kExactBelow
-
-    // part: -1 all rows; 0 q and beta; 1 k; 2 g and dO.  The second buffer is
-    // filled in parts over three steps: a wave stalls at issue while its
-    // memory queue is full, and one burst held up the step that issued it.
-    auto load_rows = [&](int64_t c0, RawRow<T, CPL> (&xq)[4], RawRow<T, CPL> (&xk)[4], RawRow<T, CPL> (&xg)[4],
-                         RawRow<T, VPL> (&xd)[4], RawScalar<T> (&xb)[4], int& xl, int part) {
-        const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-        const int r0 = 16 * ww + 4 * qg;
-        // uniform chunk bases + 32-bit per-lane offsets (64 H max(dk, dv) < 2^31
-        // is checked on the host)
-        const T* qc = qp + (c0 * rs_k + h * DK);
-        const T* kc = kp + (c0 * rs_k + h * DK);
-        const T* gc = gp + (c0 * rs_k + h * DK);
-        const T* dc = dop + (c0 * rs_v + h * dv + dv0);
-        const T* bc = bp + (c0 * H + h);
-        const unsigned sk = (unsigned)rs_k, sv = (unsigned)rs_v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (r0 + i < L) {
-                if (part <= 0) {
-                    xq[i].load(qc + ((r0 + i) * sk + CPL * cl));
-                    xb[i].load(bc + (unsigned)((r0 + i) * H));
-                }
-                if (part < 0 || part == 1) xk[i].load(kc + ((r0 + i) * sk + CPL * cl));
-                if (part < 0 || part == 2) {
-                    xg[i].load(gc + ((r0 + i) * sk + CPL * cl));
-                    xd[i].load(dc + ((r0 + i) * sv + VPL * cl));
-                }
-            } else {
-                if (part <= 0) { xq[i].zero(); xb[i].zero(); }
-                if (part < 0 || part == 1) xk[i].zero();
-                if (part < 0 || part == 2) { xg[i].zero(); xd[i].zero(); }
-            }
-        }
-        if (part <= 0) xl = L;
-    };
-    auto load_chunk = [&](int64_t c0) { load_rows(c0, rq, rk, rg, rdo, rb, Lp, -1); };
-    auto load_next = [&](int64_t c0, int part) { load_rows(c0, nrq, nrk, nrg, nrdo, nrb, nLp, part); };
-    auto take_next = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rq[i] = nrq[i]; rk[i] = nrk[i]; rg[i] = nrg[i]; rdo[i] = nrdo[i]; rb[i] = nrb[i];
-        }
-        Lp = nLp;
-    };
-    auto gate_prefix = [&](int e) {
-        V4T ltri;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ltri[j] = from_f32<T>(4 * qg + j <= cl ? 1.f : 0.f);
-        const V4T b = __builtin_bit_cast(V4T, u16x4{rg[0].x[e], rg[1].x[e], rg[2].x[e], rg[3].x[e]});
-        return mma_k16(f32x4{0.f, 0.f, 0.f, 0.f}, ltri, b);
-    };
-    auto prep_a = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) { sq += rq[i][e] * rq[i][e]; sk += rk[i][e] * rk[i][e]; }
-            sq = row16_sum(sq);
-            sk = row16_sum(sk);
-            nq[i] = __builtin_amdgcn_rsqf(sq + p.eps);   // reciprocal norms
-            nk[i] = __builtin_amdgcn_rsqf(sk + p.eps);
-            const int r = 16 * ww + 4 * qg + i;
-            beta[i] = (r < Lp) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i].f())) : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const f32x4 gp4 = gate_prefix(e);
-            if (qg == 3) sm.red[ww][CPL * cl + e] = gp4[3];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { rq[i].fence(); rk[i].fence(); rg[i].fence(); }
-    };
-    // qh Gam (hi, lo), its dO slice and Gam_C stay in registers (the state
-    // waves still read those tiles while this runs); beta kh Gam and kh/Gam
-    // (hi, lo) are written now.
-    auto prep_b = [&]() {
-        float goff[CPL];
-        bool tok = false, exact = false;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int c = CPL * cl + e;
-            float a = 0.f, tot = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const float x = sm.red[w2][c];
-                if (w2 < ww) a += x;
-                tot += x;
-            }
-            goff[e] = a;
-            xgc[e] = fast_exp2(tot * kLog2e);
-            tok |= !(tot >= kTokenBelow);
-            exact |= !(tot >= kExactBelow);
-        }
-        xtok = __builtin_amdgcn_ballot_w64(tok) != 0;
-        xexact = __builtin_amdgcn_ballot_w64(exact) != 0;
-#pragma unroll
-        for (int e4 = 0; e4 < CQ; ++e4) {
-            f32x4 G[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 gp4 = gate_prefix(4 * e4 + j);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) G[j][i] = (gp4[i] + goff[4 * e4 + j]) * kLog2e;
-            }
-            const int pc = perm32(CPL * cl + 4 * e4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * ww + 4 * qg + i;
-                const float aq = p.scale * nq[i], ai = nk[i], ak = beta[i] * ai;
-                f32x4 vq, vk, vi;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = 4 * e4 + j;
-                    const float gam = fast_exp2(G[j][i]);
-                    const float gin = fast_exp2(-G[j][i]);
-                    vq[j] = (rq[i][e] * aq) * gam;
-                    vk[j] = (rk[i][e] * ak) * gam;
-                    vi[j] = (rk[i][e] * ai) * gin;
-                }
-                xqh[i][e4] = pack4<T>(vq);
-                xql[i][e4] = pack4<T>(vq - unpack4(xqh[i][e4]));
-                *reinterpret_cast<V4T*>(&sm.kg[r * PK + pc]) = pack4<T>(vk);
-                sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], vi);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xdo[i] = rdo[i];
-    };
-
-    for (int e = tid; e < kChunk * PC; e += kWideThreads) {
-        sm.aqt[e] = from_f32<T>(0.f);    // Aqk^T blocks above the diagonal are never written
-        sm.aqtl[e] = from_f32<T>(0.f);
-    }
-    // step 3 (both groups, two of the four rows each): Ktil = (kh/Gam) Gam_C in
-    // place of kh/Gam, in the prep layout (rows 16ww+4qg+i, key columns
-    // CPL*cl..), Gam_C from LDS
-    auto ktil_in_place = [&](int i0) {
-#pragma unroll
-        for (int i = i0; i < i0 + 2; ++i) {
-            const int r = 16 * ww + 4 * qg + i;
-#pragma unroll
-            for (int e4 = 0; e4 < CQ; ++e4) {
-                const int c = CPL * cl + 4 * e4;
-                const int pc = perm32(c);
-                f32x4 x = lds4f<T>(&sm.r2[r * PK + pc]) + lds4f<T>(&sm.r3[r * PK + pc]);
-                x *= *reinterpret_cast<const f32x4*>(&sm.gc[c]);
-                sts4_split<T, true>(&sm.r2[r * PK + pc], &sm.r3[r * PK + pc], x);
-            }
-        }
-    };
-    // step 2, shared: Akk and Aqk^T, one lower-triangle block pair per item
-    auto intra_products = [&]() {
-#pragma unroll 1
-        for (int it = w; it < 10; it += 8) {
-            const int ib = it >= 6 ? 3 : (it >= 3 ? 2 : (it >= 1 ? 1 : 0));
-            const int jb = it - (ib * (ib + 1)) / 2;
-            const int ra = (16 * ib + cl) * PK + 8 * qg, rbk = (16 * jb + cl) * PK + 8 * qg;
-            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < NKB; ++kk) {
-                const V8T bh = lds8<T>(sm.r2 + rbk + 32 * kk);
-                akk = mma_k32(akk, lds8<T>(sm.kg + ra + 32 * kk), bh);
-                aqk = mma3<true>(aqk, lds8<T>(sm.r0 + ra + 32 * kk), lds8<T>(sm.r1 + ra + 32 * kk), bh,
-                                 lds8<T>(sm.r3 + rbk + 32 * kk));
-            }
-            const int s = 16 * jb + cl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * ib + 4 * qg + i;
-                const float vq = s <= r ? aqk[i] : 0.f;
-                const T hi = from_f32<T>(vq);
-                sm.aqt[kt_off(s, perm32(r))] = hi;
-                sm.aqtl[kt_off(s, perm32(r))] = from_f32<T>(vq - to_f32(hi));
-                const float vk = s < r ? akk[i] : 0.f;
-                sm.akk[r * PC + s] = from_f32<T>(vk);
-                if (ib == jb) sm.adiag[ib][4 * qg + i][cl] = vk;
-            }
-        }
-    };
-    // step 4, shared: W = (I + Akk)^{-1} beta kh Gam for key column block w; store -W^T
-    auto w_solve = [&]() {
-        if (w < DK / 16) {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            V4T tii[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tii[i] = pack4<T>(*reinterpret_cast<const f32x4*>(&sm.tdiag[i][cl][4 * qg]));
-            const int nb = 16 * w;
-            const int pc = perm32(nb + cl);
-            f32x4 X[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 acc;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = to_f32(sm.kg[(16 * i + 4 * qg + j) * PK + pc]);
-#pragma unroll
-                for (int jp = 0; jp < i; ++jp)
-                    acc = mma_k16(acc, neg4(lds4<T>(&sm.akk[(16 * i + cl) * PC + 16 * jp + 4 * qg])), pack4<T>(X[jp]));
-                X[i] = mma_k16(zero, tii[i], pack4<T>(acc));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sts4<T>(&sm.wt[kt_off(nb + cl, perm32(16 * i + 4 * qg))], -X[i]);
-        }
-    };
-
-    if (is_state) {
-        // ---------------------------------------------------------------- state waves
-        float* __restrict__ dst = reinterpret_cast<float*>(p.dst_saved);
-        const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
-        f32x4 dS[NMB];
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dS[mb][i] = p.dS_final ? p.dS_final[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] : 0.f;
-        if (nchunks > 0) lds_barrier();   // prologue
-        for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
-            const int64_t slot = t0 / kChunk + n + jc;
-            // 1: dL/dS at the end of this chunk, for the chunk-parallel gradients
-            refresh();
-            {
-                float* out = dst + (slot * H + h) * (int64_t)DK * dv;
-                const unsigned ob = (unsigned)(4 * qg * dv + vcol) * 4u;   // lane part of the byte offset
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) *atb(out, ob + (unsigned)((16 * mb + i) * dv) * 4u) = dS[mb][i];
-            }
-            lds_barrier();
-            if (__builtin_amdgcn_readfirstlane(sm.token_path)) {
-                // decay past the factorised range: the transposed recurrence token
-                // by token (no dU for this chunk: the pair-exact gradient kernel
-                // recomputes it); the prep waves' barriers are met with no work
-                refresh();
-                const int64_t c0 = t0 + jc * kChunk;
-                const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-                const TokSrc<T> src = {qp, kp, gp, bp, dop, H, h, dv, vcol, qg, p.eps, p.scale};
-                token_bwd<T, DK>(dS, src, c0, L);
-                lds_barrier();
-                lds_barrier();
-                lds_barrier();
-                lds_barrier();
-                lds_barrier();
-                continue;
-            }
-            refresh();
-            intra_products();
-            lds_barrier();
-            // 3: (I + Akk_bb)^{-1}, block b = this wave; Ktil in place
-            refresh();
-            {
-                const f32x4 na = *reinterpret_cast<const f32x4*>(&sm.adiag[ww][cl][4 * qg]);
-                f32x4 nbv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) nbv[j] = sm.adiag[ww][4 * qg + j][cl];
-                const f32x4 tw = inv_unit_lower16_x3(na, nbv, qg, cl);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.tdiag[ww][4 * qg + i][cl] = tw[i];
-            }
-            ktil_in_place(0);
-            lds_barrier();
-            refresh();
-            w_solve();
-            lds_barrier();
-            // 5a and 5b: the compiler's MFMA/LDS interleaving pattern 1 (iglp_opt)
-            // schedules these two steps 2% faster than its default (measured;
-            // the same pattern made the forward's steps 4% slower)
-            __builtin_amdgcn_iglp_opt(1);
-            // 5a: dU = Aqk^T dO + Ktil dS1
-            refresh();
-            V8T dof[2], duf[2];
-            const KtFrag kf(qg, cl);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) dof[kk] = lds8<T>(sm.dot + kt_off(16 * ww + cl, 32 * kk + 8 * qg));
-            {
-                V8T dsh[NKB], dsl[NKB];
-#pragma unroll
-                for (int kk = 0; kk < NKB; ++kk) split8<T, true>(dS[2 * kk], dS[2 * kk + 1], dsh[kk], dsl[kk]);
-                f32x4 dU[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = (i >> 1); kk < 2; ++kk) {
-                        const int ra = kf.at(i, kk);
-                        acc = mma_k32(acc, lds8<T>(sm.aqt + ra), dof[kk]);
-                        acc = mma_k32(acc, lds8<T>(sm.aqtl + ra), dof[kk]);
-                    }
-                    const int rk2 = (16 * i + cl) * PK + 8 * qg;
-#pragma unroll
-                    for (int kk = 0; kk < NKB; ++kk)
-                        acc = mma3<true>(acc, lds8<T>(sm.r2 + rk2 + 32 * kk), lds8<T>(sm.r3 + rk2 + 32 * kk), dsh[kk],
-                                         dsl[kk]);
-                    dU[i] = acc;
-                }
-                duf[0] = pack8<T>(dU[0], dU[1]);
-                duf[1] = pack8<T>(dU[2], dU[3]);
-                // dU of this chunk (fp32), for the chunk-parallel gradients, stored
-                // column-major ([dv][64]) like the forward's U
-                float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<f32x4*>(at32(ub, vcol * kChunk + 16 * i + 4 * qg)) = dU[i];
-            }
-            lds_barrier();
-            __builtin_amdgcn_iglp_opt(1);
-            // 5b: dS0 = Diag(Gam_C) dS1 + (qh Gam)^T dO - W^T dU
-            refresh();
-            const KtFrag kf2(qg, cl);
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * mb + 4 * qg]);
-                f32x4 acc = dS[mb] * gcv;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int rt = kf2.at(mb, kk);
-                    acc = mma_k32(acc, lds8<T>(sm.r0 + rt), dof[kk]);
-                    acc = mma_k32(acc, lds8<T>(sm.r1 + rt), dof[kk]);
-                    acc = mma_k32(acc, lds8<T>(sm.wt + kf2.at(mb, kk)), duf[kk]);
-                }
-                dS[mb] = acc;
-            }
-            lds_barrier();
-        }
-        if (p.dS0) {
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p.dS0[sbase + (int64_t)(16 * mb + 4 * qg + i) * dv + vcol] = dS[mb][i];
-        }
-    } else {
-        // ---------------------------------------------------------------- prep waves
-        if (nchunks > 0) {
-            const int64_t cl0 = t0 + (nchunks - 1) * kChunk;
-            load_chunk(cl0);
-            prep_a();
-            lds_barrier();
-            prep_b();
-            if (nchunks > 1) load_chunk(cl0 - kChunk);
-        }
-        for (int64_t jc = nchunks - 1; jc >= 0; --jc) {
-            const int64_t c0 = t0 + jc * kChunk;
-            // 1: the tiles held in registers
-            refresh();
-            {
-                const int pr = perm32(16 * ww + 4 * qg);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * ww + 4 * qg + i;
-#pragma unroll
-                    for (int e4 = 0; e4 < CQ; ++e4) {
-                        const int pc = perm32(CPL * cl + 4 * e4);
-                        *reinterpret_cast<V4T*>(&sm.r0[r * PK + pc]) = xqh[i][e4];
-                        *reinterpret_cast<V4T*>(&sm.r1[r * PK + pc]) = xql[i][e4];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < VPL; ++e)   // dO is an input value: its bits move as they are
-                    *reinterpret_cast<V4T*>(&sm.dot[kt_off(VPL * cl + e, pr)]) =
-                        col4(xdo[0].x, xdo[1].x, xdo[2].x, xdo[3].x, e);
-                if (ww == 0 && qg == 0) {
-#pragma unroll
-                    for (int e = 0; e < CPL; ++e) sm.gc[CPL * cl + e] = xgc[e];
-                }
-                if (ww == 0 && l == 0) {
-                    sm.token_path = xtok ? 1 : 0;
-                    if (slice == 0) p.chunk_flags[(t0 / kChunk + n + jc) * H + h] = xexact ? 1 : 0;
-                }
-            }
-            lds_barrier();
-            refresh();
-            if (jc > 1) load_next(c0 - 2 * kChunk, 0);   // rows of the chunk before the previous one
-            intra_products();
-            lds_barrier();
-            // 3: (qh Gam)^T hi/lo over the qh Gam tiles (swizzled layout); half of Ktil
-            refresh();
-            if (jc > 1) load_next(c0 - 2 * kChunk, 1);
-            {
-                const int pr = perm32(16 * ww + 4 * qg);
-#pragma unroll
-                for (int e4 = 0; e4 < CQ; ++e4) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int c = CPL * cl + 4 * e4 + j;
-                        *reinterpret_cast<V4T*>(&sm.r0[kt_off(c, pr)]) =
-                            col4(xqh[0][e4], xqh[1][e4], xqh[2][e4], xqh[3][e4], j);
-                        *reinterpret_cast<V4T*>(&sm.r1[kt_off(c, pr)]) =
-                            col4(xql[0][e4], xql[1][e4], xql[2][e4], xql[3][e4], j);
-                    }
-                }
-            }
-            ktil_in_place(2);
-            lds_barrier();
-            refresh();
-            if (jc > 1) load_next(c0 - 2 * kChunk, 2);
-            w_solve();
-            lds_barrier();
-            // 5a: norms, sigmoid and gate sums of the previous chunk
-            refresh();
-            if (jc > 0) prep_a();
-            lds_barrier();
-            // 5b: its operand values; the rows loaded in step 2 become the next ones prepared
-            refresh();
-            if (jc > 0) {
-                prep_b();
-                if (jc > 1) take_next();
-            }
-            lds_barrier();
-        }
     }
 }
 
@@ -2281,7 +1800,7 @@ template <typename T, int DK>
 static hipError_t launch_scan(const BwdParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.N * p.H * p.nslices));
     if constexpr (std::is_same<T, bf16>::value)
-        hipLaunchKernelGGL((kda_bwd_scan_bf16_kernel<DK>), grid, dim3(kWideThreads), 0, s, p);
+        return launch_scan16(p, DK, s);   // fp16 matrix-core operands (kda_scan16.hip)
     else
         hipLaunchKernelGGL((kda_bwd_scan_kernel<T, DK>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();

@@ -52,59 +52,11 @@
 #include <utility>
 
 #include "kda_device.h"
+#include "kda_f16.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace f16 {
-
-typedef _Float16 h16;
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef _Float16 hx2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mma32(f32x4 c, h8 a, h8 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(f32x4 c, h4 a, h4 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ h4 cvt4(f32x4 x) { return __builtin_convertvector(x, h4); }
-__device__ __forceinline__ h8 cvt8(f32x4 a, f32x4 b) {
-    const h4 x = cvt4(a), y = cvt4(b);
-    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-template <int N>
-__device__ __forceinline__ void cvt_store(h16* dst, const float (&x)[N]) {
-    typedef float FV __attribute__((ext_vector_type(N)));
-    typedef _Float16 HV __attribute__((ext_vector_type(N)));
-    FV v;
-#pragma unroll
-    for (int j = 0; j < N; ++j) v[j] = x[j];
-    *reinterpret_cast<HV*>(dst) = __builtin_convertvector(v, HV);
-}
-
-// Wave-wide maximum of non-negative values, as a wave-uniform value: DPP
-// within each 16-lane row, then the four row results.
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp<0x140>(v));   // row_mirror
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-// Sum over the four lanes that share l % 16 (l, l^16, l^32, l^48): every one
-// of them gets the same bits.
-__device__ __forceinline__ float qsum(float v) {
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
-}
-
-constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
 template <int DK>
 struct __attribute__((aligned(16))) Smem {

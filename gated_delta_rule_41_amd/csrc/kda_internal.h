@@ -145,6 +145,8 @@ hipError_t launch_fwd_maps(const FwdParams& p, int dk, hipStream_t stream);
 // bf16 inputs: the fused forward with fp16 matrix-core operands (kda_fwd16.hip).
 hipError_t launch_fwd16(const FwdParams& p, int out_dtype, int dk, bool save, hipStream_t stream);
 hipError_t launch_fwd16_maps(const FwdParams& p, int dk, hipStream_t stream);
+// bf16 inputs: the reverse state-gradient scan with fp16 matrix-core operands (kda_scan16.hip).
+hipError_t launch_scan16(const BwdParams& p, int dk, hipStream_t stream);
 hipError_t launch_carry(const CarryParams& p, int dk, hipStream_t stream);
 // Kernels without the chunk-start gate factorisation (kda_exact.hip): the
 // forward and the reverse scan token by token, and the chunk gradients with
