@@ -33,8 +33,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Saved per-chunk states and state gradients are fp32 for every input dtype.
-size_t state_elem_bytes(const kda_config* c) { (void)c; return 4; }
+// Saved per-chunk states and state gradients: fp32 for fp32 inputs; fp16 with
+// a power-of-two scale per 16-column group for bf16 inputs (the fp16 kernels
+// hold them as fp16-safe scaled values already).
+size_t state_elem_bytes(const kda_config* c) { return c->in_dtype == KDA_BF16 ? 2 : 4; }
+
+// The scales of the fp16 saves: one fp32 per (slot, head, 16-column group).
+size_t scale_bytes(const kda_config* c, int64_t T, int32_t N) {
+    if (c->in_dtype != KDA_BF16) return 0;
+    return (size_t)kda::num_slots(T, N) * c->H * (c->dv / 16) * sizeof(float);
+}
 
 // Config check shared by every entry point.  Returns KDA_OK or a status with
 // the reason left in g_err.
@@ -88,15 +96,15 @@ kda_status opt_ptr(const void* p, const char* name) {
     return KDA_OK;
 }
 
-// Per-chunk U (forward) and dU (reverse scan), fp32 [slots, H, 64, dv]: the
-// bf16 chunk-gradient kernel reads them instead of recomputing both.
+// Per-chunk U (forward) and dU (reverse scan), fp16 [slots, H, dv, 64] (bf16
+// inputs): the bf16 chunk-gradient kernel reads them instead of recomputing both.
 size_t chunk_u_bytes(const kda_config* c, int64_t T, int32_t N) {
     if (c->in_dtype != KDA_BF16) return 0;
-    return (size_t)kda::num_slots(T, N) * c->H * kda::kChunk * c->dv * sizeof(float);
+    return (size_t)kda::num_slots(T, N) * c->H * kda::kChunk * c->dv * 2;
 }
 
 struct SavedLayout {
-    size_t states, nq, nk, u, total;
+    size_t states, nq, nk, u, scale, total;
 };
 
 SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
@@ -107,7 +115,8 @@ SavedLayout saved_layout(const kda_config* c, int64_t T, int32_t N) {
     s.nq = align256(st);
     s.nk = s.nq + align256(nrm);
     s.u = s.nk + align256(nrm);
-    s.total = s.u + align256(chunk_u_bytes(c, T, N));
+    s.scale = s.u + align256(chunk_u_bytes(c, T, N));
+    s.total = s.scale + align256(scale_bytes(c, T, N));
     return s;
 }
 
@@ -153,8 +162,9 @@ SplitPlan split_plan(const kda_config* c, int64_t T, int32_t N) {
     return s;
 }
 
-// dL/dS at the end of every chunk (state type), then dU of every chunk, then
-// one flag per chunk and head (decay past the factorised kernels' range).
+// dL/dS at the end of every chunk (state type), then dU of every chunk, the
+// scales of both (bf16 inputs), then one flag per chunk and head (decay past
+// the factorised kernels' range).
 size_t bwd_dst_bytes(const kda_config* c, int64_t T, int32_t N) {
     return align256((size_t)kda::num_slots(T, N) * c->H * c->dk * c->dv * state_elem_bytes(c));
 }
@@ -202,7 +212,8 @@ kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q
         p.st_saved = base + L.states;
         p.nq_saved = (float*)(base + L.nq);
         p.nk_saved = (float*)(base + L.nk);
-        p.u_saved = chunk_u_bytes(cfg, T, N) ? (float*)(base + L.u) : nullptr;
+        p.u_saved = chunk_u_bytes(cfg, T, N) ? (void*)(base + L.u) : nullptr;
+        p.sv_scale = scale_bytes(cfg, T, N) ? (float*)(base + L.scale) : nullptr;
     }
     p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
     p.seqlen = cu ? 0 : (int32_t)(T / N);
@@ -309,7 +320,8 @@ size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
 
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
     if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
-    return bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)) + bwd_flag_bytes(cfg, T, N);
+    return bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)) + align256(scale_bytes(cfg, T, N)) +
+           bwd_flag_bytes(cfg, T, N);
 }
 
 kda_status kda_fwd(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k,
@@ -422,10 +434,13 @@ static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t
     p.dO = dO; p.dS_final = dSf;
     p.dst_saved = workspace;
     if (chunk_u_bytes(cfg, T, N)) {
-        p.u_saved = (const float*)(base + L.u);
-        p.du_ws = (float*)((char*)workspace + bwd_dst_bytes(cfg, T, N));
+        p.u_saved = (const void*)(base + L.u);
+        p.du_ws = (void*)((char*)workspace + bwd_dst_bytes(cfg, T, N));
+        p.sv_scale = (const float*)(base + L.scale);
+        p.ds_scale = (float*)((char*)workspace + bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)));
     }
-    p.chunk_flags = (int32_t*)((char*)workspace + bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)));
+    p.chunk_flags = (int32_t*)((char*)workspace + bwd_dst_bytes(cfg, T, N) + align256(chunk_u_bytes(cfg, T, N)) +
+                               align256(scale_bytes(cfg, T, N)));
     p.dq = dq; p.dk = dk; p.dv_out = dv; p.dg = dg; p.db = dbeta; p.dS0 = dS0;
     p.T = T; p.N = N; p.H = cfg->H; p.dv = cfg->dv;
     p.seqlen = cu ? 0 : (int32_t)(T / N);

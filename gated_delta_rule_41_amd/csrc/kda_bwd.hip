@@ -590,9 +590,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const T* __restrict__ vc = reinterpret_cast<const T*>(p.v) + c0 * rsv + h * DV;
     const T* __restrict__ doc = reinterpret_cast<const T*>(p.dO) + c0 * rsv + h * DV;
     const T* __restrict__ bc = reinterpret_cast<const T*>(p.b) + c0 * H + h;
-    const float* __restrict__ S0 = reinterpret_cast<const float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
-    const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
-    float xs0[NKV][8], xd0[NKV][8];   // S0 / dS1 row fragments (loaded during Akk and T)
+    // S0 (saved by the forward) and dS1 (left by the reverse scan): fp16 scaled by
+    // 2^-e per 16-column group, with 2^e in sv_scale / ds_scale
+    const _Float16* __restrict__ S0 = reinterpret_cast<const _Float16*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
+    const _Float16* __restrict__ dS1 = reinterpret_cast<const _Float16*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
+    const float* __restrict__ s0sc = p.sv_scale + (slot * H + h) * (DV / 16);
+    const float* __restrict__ d1sc = p.ds_scale + (slot * H + h) * (DV / 16);
+    // S0 / dS1 row fragments (loaded during Akk and T), kept in fp16 until used
+    typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+    h8v xs0[NKV], xd0[NKV];
 
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const int r0 = 16 * wl + 4 * qg;             // prep layout: rows r0..r0+3
@@ -702,7 +709,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 
     // U (saved by the forward) and dU (left by the reverse scan) of this chunk for
     // value column block 16w, accumulator layout: rows 16mb+4qg+i, column 16w+cl
-    f32x4 U[4], dU[4];
+    h4v Uh[4], dUh[4];   // fp16 as saved, converted where first used
+    f32x4 dU[4];
     RawRow<T, VPH> ddr[4], vvr[4];   // dO and v rows of this lane (prep layout), staged in LDS later
     {
     Prep P;
@@ -720,13 +728,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     lds_barrier();
     {
         if (vact) {
-            const float* __restrict__ ub = p.u_saved + (slot * H + h) * (int64_t)kChunk * DV;
-            const float* __restrict__ dub = p.du_ws + (slot * H + h) * (int64_t)kChunk * DV;
+            // fp16, scaled per 16-column group like S0 / dS1 (this wave's columns: group w)
+            const _Float16* __restrict__ ub = reinterpret_cast<const _Float16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * DV;
+            const _Float16* __restrict__ dub = reinterpret_cast<const _Float16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {   // column-major [dv][64]: four rows per 16-byte load
+            for (int mb = 0; mb < 4; ++mb) {   // column-major [dv][64]: four rows per 8-byte load
                 const int o = (16 * w + cl) * kChunk + 16 * mb + 4 * qg;
-                U[mb] = *reinterpret_cast<const f32x4*>(ub + o);
-                dU[mb] = *reinterpret_cast<const f32x4*>(dub + o);
+                Uh[mb] = *reinterpret_cast<const h4v*>(ub + o);
+                dUh[mb] = *reinterpret_cast<const h4v*>(dub + o);
             }
         }
 #pragma unroll
@@ -745,7 +754,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     if (kact) {
         const int nr = 16 * w + cl;
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) gf8(xs0[kk], S0 + (nr * DV + 32 * kk + 8 * qg));
+        for (int kk = 0; kk < NKV; ++kk) xs0[kk] = *reinterpret_cast<const h8v*>(S0 + (nr * DV + 32 * kk + 8 * qg));
     }
     // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
@@ -787,7 +796,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     if (kact) {
         const int nr = 16 * w + cl;
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) gf8(xd0[kk], dS1 + (nr * DV + 32 * kk + 8 * qg));
+        for (int kk = 0; kk < NKV; ++kk) xd0[kk] = *reinterpret_cast<const h8v*>(dS1 + (nr * DV + 32 * kk + 8 * qg));
     }
     // off-diagonal blocks, column j on wave j: T_ij = -T_ii sum_{k=j}^{i-1} Akk_ik T_kj
     {
@@ -836,9 +845,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (r0 + i) * PV + cv0) = vvr[i].x;
     }
     if (vact) {
+        const float us = s0sc[w], dus = d1sc[w];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * w, U[mb], qg, cl, true);
+            dU[mb] = __builtin_convertvector(dUh[mb], f32x4) * dus;
+            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * w, __builtin_convertvector(Uh[mb], f32x4) * us, qg, cl, true);
             put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * w, dU[mb], qg, cl, true);
         }
     }
@@ -923,10 +934,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
             V8T sh, sl, dh, dl;
+            float xs[8], xd[8];
+            const float ss = s0sc[2 * kk + (qg >> 1)], sd = d1sc[2 * kk + (qg >> 1)];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) gpart += xs0[kk][j] * xd0[kk][j];
-            cvt8(xs0[kk], sh, sl);
-            cvt8(xd0[kk], dh, dl);
+            for (int j = 0; j < 8; ++j) {
+                xs[j] = (float)xs0[kk][j] * ss;
+                xd[j] = (float)xd0[kk][j] * sd;
+                gpart += xs[j] * xd[j];
+            }
+            cvt8(xs, sh, sl);
+            cvt8(xd, dh, dl);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int r = 16 * mb + cl;

@@ -25,6 +25,8 @@
 // decay between two tokens, at most 1, so nothing overflows for any g <= 0.
 // The arithmetic is plain fp32 FMA (no matrix cores): this path is the
 // correctness path for inputs outside the factorised kernels' range.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_token.h"
@@ -173,8 +175,22 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
     const T* __restrict__ vg_ = reinterpret_cast<const T*>(p.v);
     const T* __restrict__ dog = reinterpret_cast<const T*>(p.dO);
     const T* __restrict__ bg_ = reinterpret_cast<const T*>(p.b);
-    const float* __restrict__ S0 = reinterpret_cast<const float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * DV;
-    const float* __restrict__ dS1 = reinterpret_cast<const float*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
+    // S0 and dS1: fp32 for fp32 inputs; for bf16 inputs fp16 scaled by 2^-e per
+    // 16-column group, with 2^e in sv_scale / ds_scale.  ld4 returns row c,
+    // columns j .. j + 3 (j a multiple of 4, so one group).
+    const int64_t sbase = (slot * H + h) * (int64_t)DK * DV;
+    auto ld4 = [&](const void* base, const float* scale, int c, int j) -> f32x4 {
+        if constexpr (std::is_same<T, bf16>::value) {
+            typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+            const h4v x = *reinterpret_cast<const h4v*>(reinterpret_cast<const _Float16*>(base) + sbase + (int64_t)c * DV + j);
+            return __builtin_convertvector(x, f32x4) * scale[(slot * H + h) * (DV / 16) + (j >> 4)];
+        } else {
+            (void)scale;
+            return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + sbase + (int64_t)c * DV + j);
+        }
+    };
+    auto ldS0 = [&](int c, int j) { return ld4(p.st_saved, p.sv_scale, c, j); };
+    auto ldS1 = [&](int c, int j) { return ld4(p.dst_saved, p.ds_scale, c, j); };
     auto krow = [&](int r) { return (c0 + r) * H + h; };   // token-row index into [T, H]
 
     // ================= phase 0: rows, norms, gate sums =================
@@ -221,8 +237,8 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < VPT; j += 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + v_0 + j);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(dS1 + (int64_t)c * DV + v_0 + j);
+            const f32x4 a = ldS0(c, v_0 + j);
+            const f32x4 b = ldS1(c, v_0 + j);
             d += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
         }
 #pragma unroll
@@ -348,7 +364,7 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
             #pragma unroll 1
             for (int c = 0; c < DK; ++c) {
                 const float kgv = b * sm.k[rQ * PD + c] * fast_exp(sm.G[rQ * PD + c]);
-                const f32x4 s0 = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + v0 + cQ);
+                const f32x4 s0 = ldS0(c, v0 + cQ);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) x[j] -= kgv * s0[j];
             }
@@ -402,7 +418,7 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
 #pragma unroll
             for (int i = 0; i < RA; ++i) dor[i] = *reinterpret_cast<const f32x4*>(&DUq[(rA + i) * 32 + j]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s0[e] = *reinterpret_cast<const f32x4*>(S0 + (int64_t)(cA + e) * DV + v0 + j);
+            for (int e = 0; e < 4; ++e) s0[e] = ldS0(cA + e, v0 + j);
 #pragma unroll
             for (int i = 0; i < RA; ++i)
 #pragma unroll
@@ -422,7 +438,7 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
             #pragma unroll 1
             for (int c = 0; c < DK; ++c) {
                 const float kt = sm.k[rQ * PD + c] * fast_exp(sm.gc[c] - sm.G[rQ * PD + c]);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(dS1 + (int64_t)c * DV + v0 + cQ);
+                const f32x4 d1 = ldS1(c, v0 + cQ);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) du[j] += kt * d1[j];
             }
@@ -463,8 +479,8 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                s0[e] = *reinterpret_cast<const f32x4*>(S0 + (int64_t)(cA + e) * DV + v0 + j);
-                d1[e] = *reinterpret_cast<const f32x4*>(dS1 + (int64_t)(cA + e) * DV + v0 + j);
+                s0[e] = ldS0(cA + e, v0 + j);
+                d1[e] = ldS1(cA + e, v0 + j);
             }
 #pragma unroll
             for (int i = 0; i < RA; ++i)
@@ -802,30 +818,27 @@ __global__ __launch_bounds__(kExactThreads, 1) void kda_bwd_exact_kernel(BwdPara
 }  // namespace ex
 
 // ---------------------------------------------------------------- launchers
+// fp32 inputs only: these kernels save fp32 states (bf16 inputs save fp16 ones
+// and take their token-by-token chunks inline, kda_fwd16.hip / kda_scan16.hip)
 hipError_t launch_fwd_token(const FwdParams& p, int in_dtype, int out_dtype, int dk, bool save, hipStream_t s) {
+    if (in_dtype != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(p.N * p.H * p.nslices));
-#define KDA_FWD_TOKEN(T, TO, DK)                                                                              \
-    do {                                                                                                      \
-        if (save) hipLaunchKernelGGL((ex::kda_fwd_token_kernel<T, TO, DK, true>), grid, dim3(kThreads), 0, s, p);  \
-        else hipLaunchKernelGGL((ex::kda_fwd_token_kernel<T, TO, DK, false>), grid, dim3(kThreads), 0, s, p);      \
+#define KDA_FWD_TOKEN(TO, DK)                                                                                    \
+    do {                                                                                                         \
+        if (save) hipLaunchKernelGGL((ex::kda_fwd_token_kernel<float, TO, DK, true>), grid, dim3(kThreads), 0, s, p);  \
+        else hipLaunchKernelGGL((ex::kda_fwd_token_kernel<float, TO, DK, false>), grid, dim3(kThreads), 0, s, p);      \
     } while (0)
-    if (in_dtype == 0 && out_dtype == 0) { if (dk == 128) KDA_FWD_TOKEN(float, float, 128); else KDA_FWD_TOKEN(float, float, 64); }
-    else if (in_dtype == 0) { if (dk == 128) KDA_FWD_TOKEN(float, bf16, 128); else KDA_FWD_TOKEN(float, bf16, 64); }
-    else if (out_dtype == 0) { if (dk == 128) KDA_FWD_TOKEN(bf16, float, 128); else KDA_FWD_TOKEN(bf16, float, 64); }
-    else { if (dk == 128) KDA_FWD_TOKEN(bf16, bf16, 128); else KDA_FWD_TOKEN(bf16, bf16, 64); }
+    if (out_dtype == 0) { if (dk == 128) KDA_FWD_TOKEN(float, 128); else KDA_FWD_TOKEN(float, 64); }
+    else { if (dk == 128) KDA_FWD_TOKEN(bf16, 128); else KDA_FWD_TOKEN(bf16, 64); }
 #undef KDA_FWD_TOKEN
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_scan_token(const BwdParams& p, int in_dtype, int dk, hipStream_t s) {
+    if (in_dtype != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(p.N * p.H * p.nslices));
-    if (in_dtype == 0) {
-        if (dk == 128) hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<float, 128>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<float, 64>), grid, dim3(kThreads), 0, s, p);
-    } else {
-        if (dk == 128) hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<bf16, 128>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<bf16, 64>), grid, dim3(kThreads), 0, s, p);
-    }
+    if (dk == 128) hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<float, 128>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((ex::kda_bwd_scan_token_kernel<float, 64>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

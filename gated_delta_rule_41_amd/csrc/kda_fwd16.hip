@@ -257,13 +257,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     }
                 }
                 if (SAVE) {
-                    // entering state of this chunk, fp32, true scale
-                    float* st = reinterpret_cast<float*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
+                    // entering state of this chunk: the scaled state in fp16 (|S| < 2^6
+                    // here) and 2^e of this wave's 16 columns
+                    h16* st = reinterpret_cast<h16*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
                     const unsigned lane_off = (unsigned)(qg * 4 * dv + dv0 + 16 * w + cl);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) *at32(st + (16 * mb + i) * dv, lane_off) = S[mb][i] * usc;
+                        for (int i = 0; i < 4; ++i) *at32(st + (16 * mb + i) * dv, lane_off) = (h16)S[mb][i];
+                    if (l == 0) p.sv_scale[(slot * H + h) * (dv / 16) + (dv0 >> 4) + w] = usc;
                 }
                 if (safe) {
                     h8 sf[NKB];
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         const float o = MAP ? 0.f : qsum(oo) * (p.scale / sqrtf(qsum(sqq) + p.eps)) * usc;
                         if (qg == 0) {
                             if (!MAP) op[(tok * H + h) * dv + vcol] = from_f32<TO>(o);
-                            if (SAVE) p.u_saved[((slot * H + h) * dv + vcol) * kChunk + t] = u * usc;
+                            if (SAVE) reinterpret_cast<h16*>(p.u_saved)[((slot * H + h) * dv + vcol) * kChunk + t] = (h16)u;
                         }
                     }
                 }
@@ -366,10 +368,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 uf[0] = __builtin_shufflevector(ub[0], ub[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 uf[1] = __builtin_shufflevector(ub[2], ub[3], 0, 1, 2, 3, 4, 5, 6, 7);
                 if (SAVE) {
-                    float* ubase = p.u_saved + (slot * H + h) * (int64_t)kChunk * dv;
+                    // U of this chunk in fp16, scaled like the saved state
+                    h16* ubase = reinterpret_cast<h16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * dv;
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib)
-                        *reinterpret_cast<f32x4*>(at32(ubase, vcol * kChunk + 16 * ib + 4 * qg)) = U[ib] * usc;
+                    for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<h4*>(at32(ubase, vcol * kChunk + 16 * ib + 4 * qg)) = ub[ib];
                 }
                 pend = true;
             }

@@ -60,10 +60,14 @@ struct FwdParams {
     const float* s0;     // [N,H,dk,dv] or nullptr
     void* o;             // [T,H,dv] out dtype
     float* sfinal;       // [N,H,dk,dv] or nullptr
-    void* st_saved;      // [slots,H,dk,dv] state dtype, or nullptr
+    // Saves for the backward (or nullptr).  fp32 inputs: states fp32.  bf16
+    // inputs: states and U in fp16, scaled by 2^-e per (slot, head, 16-column
+    // group), with 2^e in sv_scale.
+    void* st_saved;      // [slots,H,dk,dv]: the state entering every chunk
     float* nq_saved;     // [T,H] or nullptr
     float* nk_saved;     // [T,H] or nullptr
-    float* u_saved;      // [slots,H,dv,64] fp32 (column-major per chunk): U of every chunk (bf16 inputs), or nullptr
+    void* u_saved;       // [slots,H,dv,64] fp16 (column-major per chunk): U of every chunk (bf16 inputs)
+    float* sv_scale;     // [slots,H,dv/16] fp32: 2^e of the saved state and U (bf16 inputs)
     const int32_t* sf_dst;   // per sequence: row of sfinal to write, or -1 to skip; nullptr = itself
     int64_t T;
     int32_t N, H, dv, seqlen;
@@ -96,14 +100,17 @@ struct BwdParams {
     const void* g;
     const void* b;
     const int32_t* cu;
-    const void* st_saved;    // forward-entering state of every chunk
+    const void* st_saved;    // forward-entering state of every chunk (format as in FwdParams)
     const float* nq_saved;
     const float* nk_saved;
     const void* dO;          // [T,H,dv] in dtype
     const float* dS_final;   // [N,H,dk,dv] or nullptr
     void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
-    const float* u_saved;    // forward's U of every chunk [slots,H,dv,64] (bf16 inputs)
-    float* du_ws;            // workspace: dU of every chunk [slots,H,dv,64] (bf16 inputs)
+                             // (fp32 for fp32 inputs; fp16 scaled by ds_scale for bf16 inputs)
+    const void* u_saved;     // forward's U of every chunk [slots,H,dv,64] fp16 (bf16 inputs)
+    void* du_ws;             // workspace: dU of every chunk [slots,H,dv,64] fp16 (bf16 inputs)
+    const float* sv_scale;   // [slots,H,dv/16]: 2^e of the saved state and U (bf16 inputs)
+    float* ds_scale;         // workspace [slots,H,dv/16]: 2^e of dS1 and dU (bf16 inputs)
     int32_t* chunk_flags;    // workspace [slots,H]: 1 where the chunk's decay passes the factorised
                              // range (written by the reverse scan, read by the pair-exact kernel)
     void* dq;

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
         // ============================================================ state waves
         const int vl = 16 * w + cl;        // column inside the slice
         const int vcol = dv0 + vl;         // value column
-        float* __restrict__ dst = reinterpret_cast<float*>(p.dst_saved);
+        h16* __restrict__ dst = reinterpret_cast<h16*>(p.dst_saved);
         f32x4 dS[NMB];
         const int64_t sbase = ((int64_t)n * H + h) * DK * dv;
 #pragma unroll
@@ -194,13 +194,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                     }
                 }
                 {
-                    // dL/dS at the end of this chunk, fp32, true scale
-                    float* out = dst + (slot * H + h) * (int64_t)DK * dv;
+                    // dL/dS at the end of this chunk: the scaled values in fp16 and
+                    // 2^e of this wave's 16 columns
+                    h16* out = dst + (slot * H + h) * (int64_t)DK * dv;
                     const unsigned lane_off = (unsigned)(qg * 4 * dv + vcol);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) *at32(out + (16 * mb + i) * dv, lane_off) = dS[mb][i] * usc;
+                        for (int i = 0; i < 4; ++i) *at32(out + (16 * mb + i) * dv, lane_off) = (h16)dS[mb][i];
+                    if (l == 0) p.ds_scale[(slot * H + h) * (dv / 16) + (dv0 >> 4) + w] = usc;
                 }
                 if (safe) {
 #pragma unroll
@@ -259,11 +261,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                 }
                 yf[0] = __builtin_shufflevector(yb[0], yb[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 yf[1] = __builtin_shufflevector(yb[2], yb[3], 0, 1, 2, 3, 4, 5, 6, 7);
-                // dU of this chunk (fp32, true scale), column-major [dv][64]
-                float* ub = p.du_ws + (slot * H + h) * (int64_t)kChunk * dv;
+                // dU of this chunk in fp16 (scaled like dS1), column-major [dv][64]
+                h16* ub = reinterpret_cast<h16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * dv;
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    *reinterpret_cast<f32x4*>(at32(ub, vcol * kChunk + 16 * sb + 4 * qg)) = dU[sb] * usc;
+                for (int sb = 0; sb < 4; ++sb) *reinterpret_cast<h4*>(at32(ub, vcol * kChunk + 16 * sb + 4 * qg)) = cvt4(dU[sb]);
                 pend = true;
             }
             lds_barrier();

@@ -39,13 +39,14 @@ def test_sizes():
     cfg = _lib.make_config(32, 128, 128, KDA_BF16, KDA_F32)
     T, N = 4 * 8192, 4
     slots = T // 64 + N
-    states = slots * 32 * 128 * 128 * 4
+    states = slots * 32 * 128 * 128 * 2   # bf16 inputs: fp16 states, scaled per 16 value columns
     nrm = T * 32 * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    u = slots * 32 * 64 * 128 * 4   # per-chunk U (saved) and dU (workspace), bf16 inputs only
-    assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm) + al(u)
+    u = slots * 32 * 64 * 128 * 2   # per-chunk U (saved) and dU (workspace) in fp16, bf16 inputs only
+    sc = slots * 32 * (128 // 16) * 4   # one fp32 scale per chunk, head and 16-column group
+    assert _lib.kda_saved_size(cfg, T, N) == al(states) + 2 * al(nrm) + al(u) + al(sc)
     flags = slots * 32 * 4          # one int per chunk and head: decay past the factorised range
-    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states) + al(u) + al(flags)
+    assert _lib.kda_bwd_workspace_size(cfg, T, N) == al(states) + al(u) + al(sc) + al(flags)
     assert _lib.kda_fwd_workspace_size(cfg, T, N) == 0
     cfg32 = _lib.make_config(2, 64, 64, KDA_F32, KDA_F32)
     assert _lib.kda_saved_size(cfg32, 256, 1) == al(5 * 2 * 64 * 64 * 4) + 2 * al(256 * 2 * 4)
