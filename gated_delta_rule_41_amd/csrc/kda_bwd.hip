@@ -450,7 +450,8 @@ struct ChunkLds {
     static constexpr int RED = DGC + DK * 4;             // float[4][DK]
     static constexpr int DBV = RED + 4 * DK * 4;         // float[4][64]
     static constexpr int GW = DBV + 4 * 64 * 4;          // float[4][DK]: per-wave column sums of g
-    static constexpr int BYTES = GW + 4 * DK * 4;
+    static constexpr int SCL = GW + 4 * DK * 4;          // float[2][DV/16]: scales of S0 / dS1 (bf16 inputs)
+    static constexpr int BYTES = SCL + 2 * (DV / 16) * 4;
     static_assert(BYTES <= 163840, "chunk kernel LDS");
 };
 
@@ -563,6 +564,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     float* const sred = reinterpret_cast<float*>(lds + LY::RED);
     float* const sdbv = reinterpret_cast<float*>(lds + LY::DBV);
     float* const sgw = reinterpret_cast<float*>(lds + LY::GW);
+    float* const sscl = reinterpret_cast<float*>(lds + LY::SCL);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, qg = l >> 4, cl = l & 15;
     const int wl = w & 3, wh = w >> 2;
@@ -714,7 +716,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     RawRow<T, VPH> ddr[4], vvr[4];   // dO and v rows of this lane (prep layout), staged in LDS later
     {
     Prep P;
-    prep_fill(P, true, [] {});
+    // the 2 x DV/16 scales of S0 and dS1 go to LDS behind the first row loads, so
+    // that no later step waits on a global round trip for them
+    prep_fill(P, true, [&] {
+        if (tid < 2 * (DV / 16)) sscl[tid] = tid < DV / 16 ? s0sc[tid] : d1sc[tid - DV / 16];
+    });
     if (wl == 0 && qg == 0) {
 #pragma unroll
         for (int e = 0; e < CPH; ++e) sgc[ck0 + e] = fast_exp2(P.GC[e]);
@@ -727,13 +733,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     put_rm(P, S(4), S(4), vKG, false);   // KG  h
     lds_barrier();
     {
-        if (vact) {
-            // fp16, scaled per 16-column group like S0 / dS1 (this wave's columns: group w)
+        {
+            // fp16, scaled per 16-column group like S0 / dS1 (this wave's columns: group
+            // w).  Loaded by every wave (a wave past dv reads group 0 and never uses it):
+            // under a branch the compiler converts the halves right after the loads and
+            // so waits for them there.
+            const int wv = vact ? w : 0;
             const _Float16* __restrict__ ub = reinterpret_cast<const _Float16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * DV;
             const _Float16* __restrict__ dub = reinterpret_cast<const _Float16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {   // column-major [dv][64]: four rows per 8-byte load
-                const int o = (16 * w + cl) * kChunk + 16 * mb + 4 * qg;
+                const int o = (16 * wv + cl) * kChunk + 16 * mb + 4 * qg;
                 Uh[mb] = *reinterpret_cast<const h4v*>(ub + o);
                 dUh[mb] = *reinterpret_cast<const h4v*>(dub + o);
             }
@@ -845,7 +855,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (r0 + i) * PV + cv0) = vvr[i].x;
     }
     if (vact) {
-        const float us = s0sc[w], dus = d1sc[w];
+        const float us = sscl[w], dus = sscl[DV / 16 + w];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             dU[mb] = __builtin_convertvector(dUh[mb], f32x4) * dus;
@@ -935,7 +945,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         for (int kk = 0; kk < NKV; ++kk) {
             V8T sh, sl, dh, dl;
             float xs[8], xd[8];
-            const float ss = s0sc[2 * kk + (qg >> 1)], sd = d1sc[2 * kk + (qg >> 1)];
+            const float ss = sscl[2 * kk + (qg >> 1)], sd = sscl[DV / 16 + 2 * kk + (qg >> 1)];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 xs[j] = (float)xs0[kk][j] * ss;

@@ -60,5 +60,16 @@ __device__ __forceinline__ float qsum(float v) {
 
 constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
+
+// r * stride + add as a 32-bit VGPR offset.  The multiply is kept apart from the
+// add: fused, the compiler emits a 64-bit multiply-add whose unused upper addend
+// half can be a register a load in flight still targets, and then waits for that
+// load before issuing the next ones.
+__device__ __forceinline__ unsigned row_off(int r, int stride, int add) {
+    unsigned m = (unsigned)r * (unsigned)stride;
+    asm volatile("" : "+v"(m));
+    return m + (unsigned)add;
+}
+
 }  // namespace f16
 }  // namespace kda

@@ -408,13 +408,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
             const int sk = (int)rs_k, sv = (int)rs_v;
             // rows past the chunk end load the last row (in bounds) and are
             // zeroed where first used
-            rb.load(at32(bc, (unsigned)(min(rr, L - 1) * H)));
+            rb.load(at32(bc, row_off(min(rr, L - 1), H, 0)));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rj = min(16 * pw + 4 * qg + j, L - 1);
-                rg[j].load(at32(gc, (unsigned)(rj * sk + CPG * cl)));
+                rg[j].load(at32(gc, row_off(rj, sk, CPG * cl)));
                 if (mslice) rv[j].zero();
-                else rv[j].load(at32(vc, (unsigned)(rj * sv + 4 * cl)));
+                else rv[j].load(at32(vc, row_off(rj, sv, 4 * cl)));
             }
         };
         auto load_qk = [&](int64_t c0) {
@@ -424,8 +424,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
             const int sk = (int)rs_k;
             const int r = min(rr, L - 1);
             if (MAP) rq.zero();
-            else rq.load(at32(qc, (unsigned)(r * sk + CPL * qg)));
-            rk.load(at32(kc, (unsigned)(r * sk + CPL * qg)));
+            else rq.load(at32(qc, row_off(r, sk, CPL * qg)));
+            rk.load(at32(kc, row_off(r, sk, CPL * qg)));
         };
         if (nch > 0) {
             load_gbv(t0);
