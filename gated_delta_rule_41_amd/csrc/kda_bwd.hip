@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "kda_device.h"
+#include "kda_f16.h"
 #include "kda_internal.h"
 #include "kda_token.h"
 
@@ -557,6 +558,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     auto S = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT); };
     auto Sh = [&](int i) { return reinterpret_cast<T*>(lds + i * LY::SLOT + LY::RQ); };   // second half
     auto Sf = [&](int i) { return reinterpret_cast<float*>(lds + i * LY::SLOT); };
+    auto Sx = [&](int i) { return reinterpret_cast<_Float16*>(lds + i * LY::SLOT); };   // fp16 view
     T* const QX = reinterpret_cast<T*>(lds + LY::QX);
     float* const sbeta = reinterpret_cast<float*>(lds + LY::BETA);
     float* const sgc = reinterpret_cast<float*>(lds + LY::GC);
@@ -846,21 +848,47 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     }
     }
     lds_barrier();
-    // U rm h/l (slots 4, 3), dU rm (slot 7), dO rm (slot 6), v rm (slot 2)
+    // The value-side products meet in fp16 at one power-of-two scale per tensor:
+    // U and S0 carry per-16-column scales sv_g (those of the saved state), dU and
+    // dS1 scales ds_g; both are brought to the largest one (exact unless a value
+    // underflows, and then it is negligible against that group).  v and dO come
+    // in at 1/svmax and |scale|/dsmax, under the bounds the forward and the scan
+    // chose those scales for.  Every product below is rescaled in fp32 after.
+    float svmax = sscl[0], dsmax = sscl[DV / 16];
+#pragma unroll
+    for (int g = 1; g < DV / 16; ++g) {
+        svmax = fmaxf(svmax, sscl[g]);
+        dsmax = fmaxf(dsmax, sscl[DV / 16 + g]);
+    }
+    const float qs = fabsf(p.scale);
+    const float ko = qs > 0.f ? qs / dsmax : 0.f;           // dO -> fp16 operand
+    const float FS = svmax * dsmax;                         // U/dU/S0/dS1/v products
+    const float FO = qs > 0.f ? FS / qs : 0.f;              // products with dO
+    // U rm (slot 4), dU rm (slot 7), dO rm (slot 6), v rm (slot 2), all fp16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ddr[i].keep(r0 + i < L);
         vvr[i].keep(r0 + i < L);
-        *reinterpret_cast<decltype(ddr[i].x)*>(S(6) + (r0 + i) * PV + cv0) = ddr[i].x;
-        *reinterpret_cast<decltype(vvr[i].x)*>(S(2) + (r0 + i) * PV + cv0) = vvr[i].x;
+        f32x4 dv4, vv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { dv4[e] = ddr[i][e] * ko; vv4[e] = vvr[i][e] / svmax; }
+        *reinterpret_cast<f16::h4*>(Sx(6) + (r0 + i) * PV + cv0) = f16::cvt4(dv4);
+        *reinterpret_cast<f16::h4*>(Sx(2) + (r0 + i) * PV + cv0) = f16::cvt4(vv4);
     }
     if (vact) {
         const float us = sscl[w], dus = sscl[DV / 16 + w];
+        const float ur = us / svmax, dr = dus / dsmax;   // powers of two <= 1
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             dU[mb] = __builtin_convertvector(dUh[mb], f32x4) * dus;
-            put_blk<T, SPLIT>(S(4), S(3), PV, 16 * mb, 16 * w, __builtin_convertvector(Uh[mb], f32x4) * us, qg, cl, true);
-            put_blk<T, false>(S(7), S(7), PV, 16 * mb, 16 * w, dU[mb], qg, cl, true);
+            const f32x4 u2 = __builtin_convertvector(Uh[mb], f32x4) * ur;
+            const f32x4 d2 = __builtin_convertvector(dUh[mb], f32x4) * dr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (16 * mb + 4 * qg + i) * PV + 16 * w + cl;
+                Sx(4)[o] = (_Float16)u2[i];
+                Sx(7)[o] = (_Float16)d2[i];
+            }
         }
     }
     lds_barrier();
@@ -891,7 +919,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 const int r = 16 * mb + 4 * qg + i;
                 if (r < L) {
                     dvp[r * rv32 + nc] = from_f32<TO>(sbeta[r] * a[i]);
-                    rowpart[mb][i] += to_f32(S(2)[r * PV + nc]) * a[i];
+                    rowpart[mb][i] += (float)Sx(2)[r * PV + nc] * svmax * a[i];   // v (fp16, at 1/svmax)
                 }
             }
         }
@@ -914,23 +942,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
             const int kb = (nb + cl) * PV + 32 * kk + 8 * qg;
-            const V8T uh = lds8<T>(S(4) + kb), ul = lds8<T>(S(3) + kb);
-            const V8T vb = lds8<T>(S(2) + kb);   // rows past the chunk end are zero
+            const f16::h8 ub = *reinterpret_cast<const f16::h8*>(Sx(4) + kb);
+            const f16::h8 vb = *reinterpret_cast<const f16::h8*>(Sx(2) + kb);   // rows past the chunk end are zero
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const V8T da = lds8<T>(S(6) + (16 * mb + cl) * PV + 32 * kk + 8 * qg);
-                dAqk[mb] = mma_k32(dAqk[mb], da, uh);
-                dAqk[mb] = mma_k32(dAqk[mb], da, ul);
-                dT[mb] = mma_k32(dT[mb], lds8<T>(S(7) + (16 * mb + cl) * PV + 32 * kk + 8 * qg), vb);
+                const int ka = (16 * mb + cl) * PV + 32 * kk + 8 * qg;
+                dAqk[mb] = f16::mma32(dAqk[mb], *reinterpret_cast<const f16::h8*>(Sx(6) + ka), ub);
+                dT[mb] = f16::mma32(dT[mb], *reinterpret_cast<const f16::h8*>(Sx(7) + ka), vb);
             }
         }
-        const float bs = sbeta[nb + cl];
+        const float bs = sbeta[nb + cl] * FS;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mb + 4 * qg + i;
-                dAqk[mb][i] = nb + cl <= r ? dAqk[mb][i] : 0.f;
+                dAqk[mb][i] = nb + cl <= r ? dAqk[mb][i] * FO : 0.f;
                 dT[mb][i] *= bs;
             }
     }
@@ -943,30 +970,32 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         float gpart = 0.f;   // this lane's share of dL/dGam_C[nr] = sum_j S0[nr][j] dS1[nr][j]
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
-            V8T sh, sl, dh, dl;
-            float xs[8], xd[8];
             const float ss = sscl[2 * kk + (qg >> 1)], sd = sscl[DV / 16 + 2 * kk + (qg >> 1)];
+            f32x4 sa, sb, da_, db_;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                xs[j] = (float)xs0[kk][j] * ss;
-                xd[j] = (float)xd0[kk][j] * sd;
-                gpart += xs[j] * xd[j];
+            for (int j = 0; j < 4; ++j) {
+                sa[j] = (float)xs0[kk][j];
+                sb[j] = (float)xs0[kk][j + 4];
+                da_[j] = (float)xd0[kk][j];
+                db_[j] = (float)xd0[kk][j + 4];
+                gpart += (sa[j] * ss) * (da_[j] * sd) + (sb[j] * ss) * (db_[j] * sd);
             }
-            cvt8(xs, sh, sl);
-            cvt8(xd, dh, dl);
+            const float sr = ss / svmax, dr = sd / dsmax;   // powers of two <= 1
+            const f16::h8 s8 = f16::cvt8(sa * sr, sb * sr), d8 = f16::cvt8(da_ * dr, db_ * dr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const int r = 16 * mb + cl;
-                const V8T da = lds8<T>(S(6) + r * PV + 32 * kk + 8 * qg);
-                dQG[mb] = mma_k32(dQG[mb], da, sh);
-                dQG[mb] = mma_k32(dQG[mb], da, sl);
-                const int ka = r * PV + 32 * kk + 8 * qg;
-                dW[mb] = mma_k32(dW[mb], lds8<T>(S(7) + ka), sh);
-                dKt[mb] = mma3<true>(dKt[mb], lds8<T>(S(4) + ka), lds8<T>(S(3) + ka), dh, dl);
+                const int ka = (16 * mb + cl) * PV + 32 * kk + 8 * qg;
+                dQG[mb] = f16::mma32(dQG[mb], *reinterpret_cast<const f16::h8*>(Sx(6) + ka), s8);
+                dW[mb] = f16::mma32(dW[mb], *reinterpret_cast<const f16::h8*>(Sx(7) + ka), s8);
+                dKt[mb] = f16::mma32(dKt[mb], *reinterpret_cast<const f16::h8*>(Sx(4) + ka), d8);
             }
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) dW[mb] = -dW[mb];
+        for (int mb = 0; mb < 4; ++mb) {
+            dQG[mb] *= FO;
+            dW[mb] *= -FS;
+            dKt[mb] *= FS;
+        }
         gpart += __shfl_xor(gpart, 16);
         gpart += __shfl_xor(gpart, 32);
         if (qg == 0) sdgc[nr] = gpart;
