@@ -616,7 +616,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // g, which the first call leaves in LDS.
     struct Prep {
         RawRow<T, CPH> q[4], k[4];
-        float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4];
+        float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4], lg[4];   // lg: the beta logits
     };
     // after_loads runs once the row loads are issued, before their first use:
     // more loads issued there wait only behind these
@@ -642,6 +642,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             P.q[i].keep(ok); P.k[i].keep(ok); rg[i].keep(ok);
             // v_rcp (~1 ulp), as the forward forms beta and the reciprocal norms
             P.beta[i] = ok ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb[i])) : 0.f;
+            P.lg[i] = rb[i];
             P.iq[i] = p.scale * __builtin_amdgcn_rcpf(ok ? nq[i] : 1.f);
             P.ik[i] = __builtin_amdgcn_rcpf(ok ? nk[i] : 1.f);
         }
@@ -860,8 +861,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         svmax = fmaxf(svmax, sscl[g]);
         dsmax = fmaxf(dsmax, sscl[DV / 16 + g]);
     }
+    const float isv = 1.f / svmax, ids = 1.f / dsmax;      // exact: powers of two
     const float qs = fabsf(p.scale);
-    const float ko = qs > 0.f ? qs / dsmax : 0.f;           // dO -> fp16 operand
+    const float ko = qs * ids;                              // dO -> fp16 operand
     const float FS = svmax * dsmax;                         // U/dU/S0/dS1/v products
     const float FO = qs > 0.f ? FS / qs : 0.f;              // products with dO
     // U rm (slot 4), dU rm (slot 7), dO rm (slot 6), v rm (slot 2), all fp16
@@ -871,13 +873,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         vvr[i].keep(r0 + i < L);
         f32x4 dv4, vv4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { dv4[e] = ddr[i][e] * ko; vv4[e] = vvr[i][e] / svmax; }
+        for (int e = 0; e < 4; ++e) { dv4[e] = ddr[i][e] * ko; vv4[e] = vvr[i][e] * isv; }
         *reinterpret_cast<f16::h4*>(Sx(6) + (r0 + i) * PV + cv0) = f16::cvt4(dv4);
         *reinterpret_cast<f16::h4*>(Sx(2) + (r0 + i) * PV + cv0) = f16::cvt4(vv4);
     }
     if (vact) {
         const float us = sscl[w], dus = sscl[DV / 16 + w];
-        const float ur = us / svmax, dr = dus / dsmax;   // powers of two <= 1
+        const float ur = us * isv, dr = dus * ids;       // powers of two <= 1
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             dU[mb] = __builtin_convertvector(dUh[mb], f32x4) * dus;
@@ -914,13 +916,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 a = mma_k32(a, ah, bh[kk]);
                 a = mma_k32(a, ah, bl[kk]);
             }
+            // rows past the chunk end have v = 0 in the tile: no guard on the row sums
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mb + 4 * qg + i;
-                if (r < L) {
-                    dvp[r * rv32 + nc] = from_f32<TO>(sbeta[r] * a[i]);
-                    rowpart[mb][i] += (float)Sx(2)[r * PV + nc] * svmax * a[i];   // v (fp16, at 1/svmax)
-                }
+                rowpart[mb][i] += (float)Sx(2)[r * PV + nc] * svmax * a[i];   // v (fp16, at 1/svmax)
+                a[i] *= sbeta[r];
+            }
+            auto put = [&](int i) { *at32(dvp, (unsigned)((16 * mb + 4 * qg + i) * rv32 + nc)) = from_f32<TO>(a[i]); };
+            if (L == kChunk) {   // uniform: every row of the chunk exists
+#pragma unroll
+                for (int i = 0; i < 4; ++i) put(i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * mb + 4 * qg + i < L) put(i);
             }
         }
         // waves 0-3 write their row sums; waves 4-7 park theirs in sred (unused
@@ -937,8 +947,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     f32x4 dAqk[4], dT[4];
     if (w < 4) {
         const int nb = 16 * w;
+        // dAqkT: the same product with the operands swapped, so that the accumulator
+        // holds dAqk[16mb+cl][nb+4qg+i] and the row-major tile takes 4-element stores
+        f32x4 dAqkT[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) { dAqk[mb] = zero; dT[mb] = zero; }
+        for (int mb = 0; mb < 4; ++mb) { dAqk[mb] = zero; dT[mb] = zero; dAqkT[mb] = zero; }
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) {
             const int kb = (nb + cl) * PV + 32 * kk + 8 * qg;
@@ -947,9 +960,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int ka = (16 * mb + cl) * PV + 32 * kk + 8 * qg;
-                dAqk[mb] = f16::mma32(dAqk[mb], *reinterpret_cast<const f16::h8*>(Sx(6) + ka), ub);
+                const f16::h8 da = *reinterpret_cast<const f16::h8*>(Sx(6) + ka);
+                dAqk[mb] = f16::mma32(dAqk[mb], da, ub);
+                dAqkT[mb] = f16::mma32(dAqkT[mb], ub, da);
                 dT[mb] = f16::mma32(dT[mb], *reinterpret_cast<const f16::h8*>(Sx(7) + ka), vb);
             }
+        }
+        // dAqk rm h/l [r][s] (slots 3 and its second half; free until the last products)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            f32x4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = nb + 4 * qg + i <= 16 * mb + cl ? dAqkT[mb][i] * FO : 0.f;
+            const int o = (16 * mb + cl) * PC + nb + 4 * qg;
+            sts4_split<T, SPLIT>(S(3) + o, Sh(3) + o, x);
         }
         const float bs = sbeta[nb + cl] * FS;
 #pragma unroll
@@ -980,7 +1004,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 db_[j] = (float)xd0[kk][j + 4];
                 gpart += (sa[j] * ss) * (da_[j] * sd) + (sb[j] * ss) * (db_[j] * sd);
             }
-            const float sr = ss / svmax, dr = sd / dsmax;   // powers of two <= 1
+            const float sr = ss * isv, dr = sd * ids;       // powers of two <= 1
             const f16::h8 s8 = f16::cvt8(sa * sr, sb * sr), d8 = f16::cvt8(da_ * dr, db_ * dr);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
@@ -1049,17 +1073,22 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            f32x4 a = zero;
+            // a: dAkk[16mb+4qg+i][nb+cl]; at: operands swapped, dAkk[16mb+cl][nb+4qg+i]
+            f32x4 a = zero, at = zero;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                a = mma_k32(a, lds8<T>(Sh(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg),
-                            lds8<T>(S(5) + (nb + cl) * PC + 32 * kk + 8 * qg));
+            for (int kk = 0; kk < 2; ++kk) {
+                const V8T xa = lds8<T>(Sh(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
+                const V8T tb = lds8<T>(S(5) + (nb + cl) * PC + 32 * kk + 8 * qg);
+                a = mma_k32(a, xa, tb);
+                at = mma_k32(at, tb, xa);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mb + 4 * qg + i;
-                a[i] = nb + cl < r ? -a[i] : 0.f;
+                a[i] = nb + cl < 16 * mb + 4 * qg + i ? -a[i] : 0.f;
+                at[i] = nb + 4 * qg + i < 16 * mb + cl ? -at[i] : 0.f;
             }
-            dAkk[mb] = a;
+            sts4<T>(QX + (nb + cl) * PC + 16 * mb + 4 * qg, a);   // dAkk^T [s][r]
+            dAkk[mb] = at;
         }
     }
     lds_barrier();
@@ -1070,10 +1099,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, dAkk[mb], qg, cl, true);
-            put_blk<T, false>(QX, QX, PC, 16 * mb, nb, dAkk[mb], qg, cl, false);
-            put_blk<T, SPLIT>(S(3), Sh(3), PC, 16 * mb, nb, dAqk[mb], qg, cl, true);
-            put_blk<T, SPLIT>(S(7), Sh(7), PC, 16 * mb, nb, dAqk[mb], qg, cl, false);
+            sts4<T>(Sh(0) + (16 * mb + cl) * PC + nb + 4 * qg, dAkk[mb]);   // dAkk rm [r][s]
+            const int o = (nb + cl) * PC + 16 * mb + 4 * qg;                // dAqk^T h/l [s][r]
+            sts4_split<T, SPLIT>(S(7) + o, Sh(7) + o, dAqk[mb]);
         }
     }
     put_tp(P, S(2), S(6), vKI, true);
@@ -1156,7 +1184,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         const float aq = P.iq[i], ai = P.ik[i];
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
-            const float gam = fast_exp2(P.G[i][e]), gin = fast_exp2(-P.G[i][e]), ek = fast_exp2(P.GC[e] - P.G[i][e]);
+            const float gam = fast_exp2(P.G[i][e]), gin = fast_exp2(-P.G[i][e]), ek = sgc[ck0 + e] * gin;
             const float qh = P.q[i][e] * aq, kh = P.k[i][e] * ai;
             const float QG = qh * gam, KGv = P.beta[i] * kh * gam, KIv = kh * gin, Ktv = kh * ek;
             dqh[i][e] = gQ[i][e] * gam;
@@ -1167,12 +1195,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         }
     }
     lds_barrier();   // F0 reads done before it holds the row sums below
+    // per-lane column partials [4 row blocks][4 row groups][DK] (summed after the
+    // barrier in a fixed order; no cross-lane shuffles on this path)
+    float* const spart = F0 + 512;
+    typedef float FC __attribute__((ext_vector_type(CPH)));   // the lane's CPH columns
+    {
+        FC v;
 #pragma unroll
-    for (int e = 0; e < CPH; ++e) {
-        float s = colp[e];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        if (qg == 0) sred[wl * DK + ck0 + e] = s;
+        for (int e = 0; e < CPH; ++e) v[e] = colp[e];
+        *reinterpret_cast<FC*>(&spart[(wl * 4 + qg) * DK + ck0]) = v;
     }
     // per-half row sums: qh . dqh, kh . dkh, and the k part of dbeta
     float* const srow = F0;   // [2 halves][3][64]
@@ -1191,40 +1222,40 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         }
     }
     lds_barrier();
-    float dGC[CPH];
+    FC dGC = *reinterpret_cast<const FC*>(&spart[ck0]);
 #pragma unroll
-    for (int e = 0; e < CPH; ++e) {
-        const int c = ck0 + e;
-        dGC[e] = sred[c] + sred[DK + c] + sred[2 * DK + c] + sred[3 * DK + c] + sdgc[c] * sgc[c];
-    }
-    lds_barrier();
+    for (int g = 1; g < 16; ++g) dGC += *reinterpret_cast<const FC*>(&spart[g * DK + ck0]);
+    dGC += *reinterpret_cast<const FC*>(&sdgc[ck0]) * *reinterpret_cast<const FC*>(&sgc[ck0]);
     {
-        float suf[CPH];
+        // reverse cumsum of dG over the 64 rows: the lane's own four rows, then the
+        // totals of every later row group (row 16 wl + 4 qg + i), from LDS
+        float* const stot = F0 + 512 + 16 * DK;
+        FC tot;
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
             float a = 0.f;
 #pragma unroll
             for (int i = 3; i >= 0; --i) { a += dG[i][e]; dG[i][e] = a; }
-            const float tot = a;
-            float s = tot, x;
-            x = __shfl_down(s, 16);
-            if (qg <= 2) s += x;
-            x = __shfl_down(s, 32);
-            if (qg <= 1) s += x;
-            suf[e] = s - tot;
-            if (qg == 0) sred[wl * DK + ck0 + e] = s;
+            tot[e] = a;
         }
+        *reinterpret_cast<FC*>(&stot[(wl * 4 + qg) * DK + ck0]) = tot;
         lds_barrier();
+        FC a = dGC;
+        const int wlu = __builtin_amdgcn_readfirstlane(wl);   // the row block is wave-uniform
 #pragma unroll
-        for (int e = 0; e < CPH; ++e) {
-            const int c = ck0 + e;
-            float a = suf[e] + dGC[e];
+        for (int w2 = 0; w2 < 4; ++w2) {
+            if (w2 < wlu) continue;
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2)
-                if (w2 > wl) a += sred[w2 * DK + c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dG[i][e] += a;
+            for (int q2 = 0; q2 < 4; ++q2) {
+                const FC v = *reinterpret_cast<const FC*>(&stot[(w2 * 4 + q2) * DK + ck0]);
+                if (w2 > wlu) a += v;
+                else a += q2 > qg ? v : FC(0.f);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < CPH; ++e) dG[i][e] += a[e];
     }
     // ================= through the L2 norms and the sigmoid; write =================
     TO* __restrict__ dqp = reinterpret_cast<TO*>(p.dq) + c0 * rsk + h * DK;
@@ -1232,10 +1263,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     TO* __restrict__ dgp = reinterpret_cast<TO*>(p.dg) + c0 * rsk + h * DK;
     TO* __restrict__ dbp = reinterpret_cast<TO*>(p.db) + c0 * H + h;
     const float isc2 = p.scale != 0.f ? 1.f / (p.scale * p.scale) : 0.f;
+    const bool full = L == kChunk;   // uniform
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
-        if (r < L) {
+        if (full || r < L) {
             const float aq = P.iq[i], ai = P.ik[i];
             const float sq = srow[0 * 64 + r] + srow[3 * 64 + r];
             const float sk = srow[1 * 64 + r] + srow[4 * 64 + r];
@@ -1254,8 +1286,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             if (wh == 0 && cl == 0) {
                 const float db = srow[2 * 64 + r] + srow[5 * 64 + r];
                 const float dbeta = db + sdbv[r] + sdbv[64 + r] + sdbv[128 + r] + sdbv[192 + r];
-                // sigma'(b) from the logit itself (reloaded: one value per row)
-                dbp[r * H] = from_f32<TO>(dbeta * sigmoid_deriv(gload1(bc + r * H)));
+                // sigma'(b) from the logit itself
+                dbp[r * H] = from_f32<TO>(dbeta * sigmoid_deriv(P.lg[i]));
             }
         }
     }
