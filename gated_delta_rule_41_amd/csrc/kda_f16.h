@@ -61,6 +61,17 @@ __device__ __forceinline__ float qsum(float v) {
 constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
 
+// Four 16-bit values through the LDS transpose read (ds_read_b64_tr_b16): every
+// lane names 8 bytes, and inside each row of 16 lanes lane t receives element
+// (t & 3) of the 8 bytes named by lanes 4k + (t >> 2), k = 0..3 (the layout as
+// measured on gfx950).  A row-major [r][c] tile read with lane l of a row naming
+// (r0 + (l >> 2), c0 + 4 (l & 3)) gives lane t the column c0 + t, rows r0..r0+3.
+__device__ __forceinline__ h4 lds_tr4(const h16* p) {
+    typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<h16*>(p)));
+    return __builtin_bit_cast(h4, r);
+}
+
 // r * stride + add as a 32-bit VGPR offset.  The multiply is kept apart from the
 // add: fused, the compiler emits a 64-bit multiply-add whose unused upper addend
 // half can be a register a load in flight still targets, and then waits for that

@@ -64,6 +64,7 @@ struct __attribute__((aligned(16))) Smem {
     static constexpr int PC = kChunk + 8;  // row stride of [64][64] tiles
     static constexpr int PV = kChunk + 8;  // row stride of the transposed v tile
     static constexpr int TDS = 20;         // row stride of a 16x16 diagonal inverse
+    static constexpr int PKT = DK + 16;    // row stride of the row-major Ktil tile (rows 8 banks apart)
     // single-buffered: read by the state waves in the first phase of a chunk,
     // rewritten by the prep waves in the second
     h16 qg[kChunk * PK];          // qh 2^G                       [r][perm32(c)]
@@ -71,7 +72,7 @@ struct __attribute__((aligned(16))) Smem {
     struct Buf {
         unsigned short vt[kSlice * PV];   // v (bf16 bits) transposed  [j][r]
         float beta[kChunk];
-        h16 kt[DK * kChunk];      // (kh 2^(G_C - G))^T           kt_off(c, perm32(r))
+        h16 kt[kChunk * PKT];     // kh 2^(G_C - G), row-major    [r][c] (read transposed)
         h16 aqk[kChunk * PC];     // lower(Aqk)                   [r][perm32(s)]
         h16 nakk[kChunk * PC];    // -Akk, off-diagonal blocks    [r][s]
         h16 td[4][16 * TDS];      // (I + Akk_bb)^{-1}            [b][r][s]
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
     typedef bf16 T;
     typedef Smem<DK> SM;
     __shared__ SM sm;
-    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, TDS = SM::TDS;
+    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, TDS = SM::TDS, PKT = SM::PKT;
     constexpr int CPL = DK / 4;     // key channels per prep lane (row layout)
     constexpr int CPG = DK / 16;    // key channels per prep lane (gate column layout)
     constexpr int NKB = DK / 32;    // k32 steps over dk
@@ -194,14 +195,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                             if (r < Lp) *at32(ob + (int64_t)(16 * ib + i) * rs_v, lane_off) = from_f32<TO>(O[ib][i] * ousc);
                         }
                 }
-                const KtFrag kf(qg, cl);
+                // Ktil^T fragments by transpose reads of the row-major tile: lane
+                // (qg, cl) gets channel 16mb + cl of rows 32kk + 16h + 4qg .. + 3,
+                // positions 8qg + 4h + j (the perm32 order of uf)
+                const h16* kb = &B.kt[(4 * qg + (cl >> 2)) * PKT + 4 * (cl & 3)];
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
                     const f32x4 gcv = *reinterpret_cast<const f32x4*>(&B.gamc[16 * mb + 4 * qg]);
                     S[mb] *= gcv;
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-                        S[mb] = mma32(S[mb], *reinterpret_cast<const h8*>(&B.kt[kf.at(mb, kk)]), uf[kk]);
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const h4 lo = lds_tr4(kb + (32 * kk) * PKT + 16 * mb);
+                        const h4 hi = lds_tr4(kb + (32 * kk + 16) * PKT + 16 * mb);
+                        S[mb] = mma32(S[mb], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), uf[kk]);
+                    }
                 }
                 pend = false;
             }
@@ -606,12 +613,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 f32x4 aoff[3][2];
 #pragma unroll
                 for (int jb = 0; jb < 3; ++jb) aoff[jb][0] = aoff[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // identity halves for the Ktil transpose: B[k = 8qg+j][n = cl] = (k == n + 16hh)
-                h8 eye[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) eye[hh][j] = (h16)((8 * qg + j == cl + 16 * hh) ? 1.f : 0.f);
                 h8 aqs[2], aks[2];   // (dk = 128) fragments 0 and 1, written beside 2 and 3
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk) {
@@ -666,16 +667,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                             *reinterpret_cast<h4*>(dk + pos) = b;
                         }
                     }
-                    // Ktil^T through the matrix core: A = this lane's Ktil fragment,
-                    // B = an identity half, so lane (qg', cl') receives rows
-                    // 16pw+4qg'+i of the channel in k-slot cl'+16hh
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const f32x4 d = mma32(f32x4{0.f, 0.f, 0.f, 0.f}, kt8, eye[hh]);
-                        const int ks = cl + 16 * hh;
-                        const int c = CPL * (ks >> 3) + 8 * kk + (ks & 7);
-                        *reinterpret_cast<h4*>(&B.kt[kt_off(c, perm32(16 * pw + 4 * qg))]) = cvt4(d);
-                    }
+                    // Ktil, row-major (the state waves read it transposed)
+                    *reinterpret_cast<h8*>(&B.kt[rr * PKT + CPL * qg + 8 * kk]) = kt8;
                     // off-diagonal products of this fragment
                     h8 f = (h8)(h16)1.f;   // running factor from block pw-1 down
 #pragma unroll
