@@ -43,14 +43,15 @@ struct __attribute__((aligned(16))) ScanSmem16 {
     static constexpr int PC = kChunk + 8;  // row stride of [64][64] tiles
     static constexpr int PV = kChunk + 8;  // row stride of the transposed dO tile
     static constexpr int TDS = 20;         // row stride of a 16x16 diagonal block
+    static constexpr int PKT = DK + 16;    // row stride of the row-major qh 2^G / beta kh 2^G tiles
     // single-buffered: read by the state waves in the first phase of a chunk,
     // rewritten by the prep waves in the second
     h16 ktr[kChunk * PK];         // kh 2^(G_C - G)               [r][perm32(c)]
     h16 aqt[kChunk * PC];         // Aqk^T                        [s][perm32(r)]  (blocks r < s stay 0)
     struct Buf {
         unsigned short dot[kSlice * PV];  // dO (bf16 bits) transposed     [j][perm32(r)]
-        h16 qgt[DK * kChunk];     // (qh 2^G)^T                   kt_off(c, perm32(r))
-        h16 nkgt[DK * kChunk];    // -(beta kh 2^G)^T             kt_off(c, perm32(r))
+        h16 qgt[kChunk * PKT];    // qh 2^G, row-major            [r][c] (read transposed)
+        h16 nkgt[kChunk * PKT];   // -beta kh 2^G, row-major      [r][c] (read transposed)
         h16 nakt[kChunk * PC];    // -Akk^T, off-diagonal blocks  [s][r]
         h16 tdt[4][16 * TDS];     // ((I + Akk_bb)^{-1})^T        [b][s][r]
         float gamc[DK];           // 2^G_C
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
     typedef bf16 T;
     typedef ScanSmem16<DK> SM;
     __shared__ SM sm;
-    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, TDS = SM::TDS;
+    constexpr int PK = SM::PK, PC = SM::PC, PV = SM::PV, TDS = SM::TDS, PKT = SM::PKT;
     constexpr int CPL = DK / 4;     // key channels per prep lane (row layout)
     constexpr int CPG = DK / 16;    // key channels per prep lane (gate column layout)
     constexpr int NKB = DK / 32;    // k32 steps over dk
@@ -133,15 +134,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
             if (pend) {
                 // dS0 = Diag(2^G_C) dS1 + (qh 2^G)^T dO - (beta kh 2^G)^T Y
                 const typename SM::Buf& B = sm.buf[(it - 1) & 1];
-                const KtFrag kf(qg, cl);
+                // transposed fragments by LDS transpose reads of the row-major tiles:
+                // lane (qg, cl) gets channel 16mb + cl of rows 32kk + 16h + 4qg .. + 3
+                const int fo = (4 * qg + (cl >> 2)) * PKT + 4 * (cl & 3);
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
                     const f32x4 gcv = *reinterpret_cast<const f32x4*>(&B.gamc[16 * mb + 4 * qg]);
                     dS[mb] *= gcv;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        dS[mb] = mma32(dS[mb], *reinterpret_cast<const h8*>(&B.qgt[kf.at(mb, kk)]), dof[kk]);
-                        dS[mb] = mma32(dS[mb], *reinterpret_cast<const h8*>(&B.nkgt[kf.at(mb, kk)]), yf[kk]);
+                        const int o0 = fo + (32 * kk) * PKT + 16 * mb, o1 = o0 + 16 * PKT;
+                        const h8 aq = __builtin_shufflevector(lds_tr4(&B.qgt[o0]), lds_tr4(&B.qgt[o1]), 0, 1, 2, 3, 4, 5, 6, 7);
+                        const h8 ak = __builtin_shufflevector(lds_tr4(&B.nkgt[o0]), lds_tr4(&B.nkgt[o1]), 0, 1, 2, 3, 4, 5, 6, 7);
+                        dS[mb] = mma32(dS[mb], aq, dof[kk]);
+                        dS[mb] = mma32(dS[mb], ak, yf[kk]);
                     }
                 }
                 pend = false;
@@ -466,11 +472,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                 f32x4 aoff[3][2];
 #pragma unroll
                 for (int jb = 0; jb < 3; ++jb) aoff[jb][0] = aoff[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                h8 eye[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) eye[hh][j] = (h16)((8 * qg + j == cl + 16 * hh) ? 1.f : 0.f);
                 h8 kts[2];   // (dk = 128) fragments 0 and 1, written beside 2 and 3
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk) {
@@ -513,15 +514,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                             *reinterpret_cast<h4*>(dkt + pos) = a;
                         }
                     }
-                    // (qh 2^G)^T and -(beta kh 2^G)^T through the matrix core
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int ks = cl + 16 * hh;
-                        const int c = CPL * (ks >> 3) + 8 * kk + (ks & 7);
-                        const int o = kt_off(c, perm32(16 * pw + 4 * qg));
-                        *reinterpret_cast<h4*>(&B.qgt[o]) = cvt4(mma32(f32x4{0.f, 0.f, 0.f, 0.f}, aq, eye[hh]));
-                        *reinterpret_cast<h4*>(&B.nkgt[o]) = cvt4(mma32(f32x4{0.f, 0.f, 0.f, 0.f}, ak, eye[hh]));
-                    }
+                    // qh 2^G and -beta kh 2^G row-major (the state waves read them transposed)
+                    *reinterpret_cast<h8*>(&B.qgt[rr * PKT + CPL * qg + 8 * kk]) = aq;
+                    *reinterpret_cast<h8*>(&B.nkgt[rr * PKT + CPL * qg + 8 * kk]) = ak;
                     h8 f = (h8)(h16)1.f;
 #pragma unroll
                     for (int jb = pw - 1; jb >= 0; --jb) {
