@@ -61,6 +61,21 @@ __device__ __forceinline__ float qsum(float v) {
 constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
 
+// A 16x16 fp32 block in the accumulator layout (lane (qg, cl): rows 4qg + i,
+// column cl) as fp16 rows: the block enters the matrix core as the A operand
+// against an identity B (eye[j] = (4qg + j == cl)), which hands lane (qg, cl)
+// row cl, columns 4qg .. 4qg + 3 -- four consecutive elements for one store.
+// Exact: fp16 values times one.
+__device__ __forceinline__ h4 block_rows4(f32x4 x, h4 eye) {
+    return cvt4(mma16(f32x4{0.f, 0.f, 0.f, 0.f}, cvt4(x), eye));
+}
+__device__ __forceinline__ h4 block_eye4(int qg, int cl) {
+    h4 e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = (h16)((4 * qg + j == cl) ? 1.f : 0.f);
+    return e;
+}
+
 // Four 16-bit values through the LDS transpose read (ds_read_b64_tr_b16): every
 // lane names 8 bytes, and inside each row of 16 lanes lane t receives element
 // (t & 3) of the 8 bytes named by lanes 4k + (t >> 2), k = 0..3 (the layout as
