@@ -535,6 +535,21 @@ __device__ __forceinline__ void store_row(TO* p, const float (&v)[N]) {
     }
 }
 
+// The A fragment (8 positions, perm32 order) of T^T at rows 16mb + cl and
+// contraction block 32kk, read straight from the row-major T tile with the LDS
+// transpose load (ds_read_b64_tr_b16: inside each row of 16 lanes, lane t
+// receives element (t & 3) of the 8 bytes named by lanes 4k + (t >> 2),
+// k = 0..3, as measured on gfx950): lane l names row 32kk + 16h + 4qg + (l >> 2),
+// columns 16mb + 4(l & 3), so lane cl gets T[32kk + 16h + 4qg + j][16mb + cl].
+__device__ __forceinline__ bf16x8 lds_trT(const bf16* tile, int ld, int mb, int kk, int qg, int cl) {
+    typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+    const bf16* p0 = tile + (32 * kk + 4 * qg + (cl >> 2)) * ld + 16 * mb + 4 * (cl & 3);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<bf16*>(p0)));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(const_cast<bf16*>(p0 + 16 * ld)));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ============================================================================
 // B2 for bf16 inputs with 8 waves.
 //
@@ -835,16 +850,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         else if (w == 2) solve_col(std::integral_constant<int, 2>{});
     }
     lds_barrier();
-    // T tiles: Trm [r][s] (slot 5 first half), T^T [s][perm32(r)] (slot 0 first half); KG^T [c][s] (slot 1)
+    // T tile: Trm [r][s] (slot 0 first half, kept until the last products; its
+    // transpose is read with the LDS transpose load), eight elements per thread;
+    // KG^T [c][s] (slot 1)
     {
-        T* const Trm = S(5);
-        T* const Ttp = S(0);
-        for (int e = tid; e < kChunk * kChunk; e += kWideThreads) {
-            const int r = e >> 6, c = e & 63;
-            const float t = Tf[r * PF + c];
-            Trm[r * PC + c] = from_f32<T>(t);
-            Ttp[c * PC + perm32(r)] = from_f32<T>(t);
-        }
+        static_assert(kChunk * kChunk == 8 * kWideThreads, "one 8-element row piece per thread");
+        const int r = tid >> 3, c = 8 * (tid & 7);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&Tf[r * PF + c]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&Tf[r * PF + c + 4]);
+        *reinterpret_cast<V8T*>(S(0) + r * PC + c) = pack8<T>(a, b);
         put_tp(P, S(1), S(1), vKG, false);
     }
     }
@@ -912,7 +926,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             f32x4 a = zero;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const V8T ah = lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
+                const V8T ah = lds_trT(S(0), PC, mb, kk, qg, cl);   // T^T
                 a = mma_k32(a, ah, bh[kk]);
                 a = mma_k32(a, ah, bl[kk]);
             }
@@ -1062,7 +1076,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         for (int mb = 0; mb < 4; ++mb) {
             f32x4 x = zero;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) x = mma_k32(x, lds8<T>(S(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg), th[kk]);
+            for (int kk = 0; kk < 2; ++kk) x = mma_k32(x, lds_trT(S(0), PC, mb, kk, qg, cl), th[kk]);
             put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, x, qg, cl, true);
         }
     }
@@ -1078,7 +1092,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const V8T xa = lds8<T>(Sh(0) + (16 * mb + cl) * PC + 32 * kk + 8 * qg);
-                const V8T tb = lds8<T>(S(5) + (nb + cl) * PC + 32 * kk + 8 * qg);
+                const V8T tb = lds8<T>(S(0) + (nb + cl) * PC + 32 * kk + 8 * qg);
                 a = mma_k32(a, xa, tb);
                 at = mma_k32(at, tb, xa);
             }
@@ -1121,7 +1135,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = (nb + cl) * PC + 32 * kk + 8 * qg;
-                a = mma_k32(a, lds8<T>(S(0) + ka), whi[kk]);                                 // T^T dW
+                a = mma_k32(a, lds_trT(S(0), PC, mb, kk, qg, cl), whi[kk]);                  // T^T dW
                 const V8T kih = lds8<T>(S(2) + kb);
                 a = mma_k32(a, lds8<T>(Sh(0) + ka), kih);                                    // dAkk KI
                 qq = mma3<true>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + ka), kih, lds8<T>(S(6) + kb));   // dAqk KI
