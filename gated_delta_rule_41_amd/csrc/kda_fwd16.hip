@@ -82,6 +82,8 @@ struct __attribute__((aligned(16))) Smem {
     float etot[4][DK];            // 2^(block decay) per 16-row block
     h16 etoth[4][DK];             //   the same in fp16
     h16 kcol[3][16 * PK];         // blocks 0-2: kh 2^(G_b - G) (column operands), fragment order
+    h8 ninv[4][64];               // per block, per lane: the A and B fragments of its strictly
+                                  // lower diagonal block N (the state waves invert I + N)
 };
 
 template <typename TO, int DK, bool SAVE, bool MAP>
@@ -384,6 +386,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 }
                 pend = true;
             }
+            if (it + 1 < nch) {
+                // (I + N)^{-1} of row block w of chunk it+1, N from the prep wave of that
+                // block: (I - N)(I + N^2)(I + N^4)(I + N^8), every product one fp16 k16
+                // product; X and X^T carried as accumulator pairs (the accumulator of X
+                // is the B operand of X and the A operand of X^T); T^T comes out in the
+                // accumulator layout
+                const h8 nn = sm.ninv[w][l];
+                const h4 na = __builtin_shufflevector(nn, nn, 0, 1, 2, 3);   // A operand of N
+                const h4 nb = __builtin_shufflevector(nn, nn, 4, 5, 6, 7);   // B operand of N
+                f32x4 eyev;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) eyev[i] = (4 * qg + i == cl) ? 1.f : 0.f;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 p2 = mma16(z, na, nb);
+                const f32x4 p2t = mma16(z, nb, na);
+                const h4 p2h = cvt4(p2), p2th = cvt4(p2t);
+                const f32x4 p4 = mma16(z, p2th, p2h);
+                const f32x4 p4t = mma16(z, p2h, p2th);
+                const h4 p4h = cvt4(p4), p4th = cvt4(p4t);
+                const f32x4 p8 = mma16(z, p4th, p4h);
+                const f32x4 y = mma16(eyev + p4 + p8, p4th, cvt4(p8));
+                const f32x4 zz = mma16(y, p2th, cvt4(y));
+                const f32x4 tt = mma16(z, cvt4(zz), cvt4(eyev - __builtin_convertvector(na, f32x4)));   // (I-N)^T
+                *reinterpret_cast<h4*>(&sm.buf[(it + 1) & 1].td[w][cl * TDS + 4 * qg]) = cvt4(tt);
+            }
             lds_barrier();
         }
         const int nd = p.sf_dst ? p.sf_dst[n] : n;   // the row of sfinal this sequence ends
@@ -571,28 +598,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     d2[i] = cl < sI ? d2[i] : 0.f;    // N
                     d3[i] = sI <= cl ? d3[i] : 0.f;
                 }
-                // diagonal block inverse (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
-                // every product one fp16 k16 product; X and X^T carried as accumulator
-                // pairs (the accumulator of X is the B operand of X and the A operand
-                // of X^T); returns T^T in accumulator layout
-                {
-                    f32x4 eyev;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) eyev[i] = (4 * qg + i == cl) ? 1.f : 0.f;
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    const h4 na = cvt4(d1), nb = cvt4(d2);   // A and B operands of N
-                    const f32x4 p2 = mma16(z, na, nb);
-                    const f32x4 p2t = mma16(z, nb, na);
-                    const h4 p2h = cvt4(p2), p2th = cvt4(p2t);
-                    const f32x4 p4 = mma16(z, p2th, p2h);
-                    const f32x4 p4t = mma16(z, p2h, p2th);
-                    const h4 p4h = cvt4(p4), p4th = cvt4(p4t);
-                    const f32x4 p8 = mma16(z, p4th, p4h);
-                    const f32x4 y = mma16(eyev + p4 + p8, p4th, cvt4(p8));
-                    const f32x4 zz = mma16(y, p2th, cvt4(y));
-                    const f32x4 tt = mma16(z, cvt4(zz), cvt4(eyev - d1));   // (I-N)^T
-                    *reinterpret_cast<h4*>(&B.td[pw][cl * TDS + 4 * qg]) = cvt4(tt);
-                }
+                // the diagonal block N as the A and B fragments of the inverse, which
+                // state wave pw forms in phase B (it has the time there)
+                sm.ninv[pw][l] = __builtin_shufflevector(cvt4(d1), cvt4(d2), 0, 1, 2, 3, 4, 5, 6, 7);
                 if (SAVE && slice == 0 && qg == 0 && rr < Lm) {
                     p.nq_saved[(cm + rr) * H + h] = nq;
                     p.nk_saved[(cm + rr) * H + h] = nk;
