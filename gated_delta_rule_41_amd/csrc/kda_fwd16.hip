@@ -505,17 +505,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     const u16x4 x = {rv[0].x[ee], rv[1].x[ee], rv[2].x[ee], rv[3].x[ee]};
                     *reinterpret_cast<u16x4*>(&B.vt[(4 * cl + ee) * PV + 16 * pw + 4 * qg]) = x;
                 }
+                // 1/||q||, 1/||k|| and the sigmoid by the hardware reciprocal
+                // (square root), ~1 ulp: the operands they scale are rounded to
+                // fp16 (11 bits)
                 float sq = 0.f, sk = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     sq += rq[c] * rq[c];
                     sk += rk[c] * rk[c];
                 }
-                const float nq = sqrtf(qsum(sq) + p.eps);
-                const float nk = sqrtf(qsum(sk) + p.eps);
+                const float ssq = qsum(sq) + p.eps;
+                const float ssk = qsum(sk) + p.eps;
                 // (the query scale is applied to O, which is linear in qh)
-                const float rqs = 1.f / nq, rkk = 1.f / nk;
-                const float beta = (rr < Lm) ? 1.f / (1.f + fast_exp(-rb.f())) : 0.f;
+                const float rqs = __builtin_amdgcn_rsqf(ssq), rkk = __builtin_amdgcn_rsqf(ssk);
+                const float beta = (rr < Lm) ? __builtin_amdgcn_rcpf(1.f + fast_exp(-rb.f())) : 0.f;
                 if (qg == 0) B.beta[rr] = beta;
                 // block-local inclusive prefix of g over the wave's 16 rows, as one
                 // k16 product per column group (exact bf16 products, fp32 sums); it
@@ -543,27 +546,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 const bool bad = !(gmin >= kUnsafe) || !(gmax <= 0.f);
                 const bool anybad = __builtin_amdgcn_ballot_w64(bad) != 0;
                 if (l == 0) B.flag[pw] = anybad ? 1 : 0;
-                // 2^(block total) per channel: the last row's prefix goes through
-                // LDS (same wave, in order) so that each lane exponentiates two
-                if (cl == 15) {
-#pragma unroll
-                    for (int c = 0; c < CPL; c += 4)
-                        *reinterpret_cast<f32x4*>(&sm.etot[pw][CPL * qg + c]) =
-                            f32x4{Gl[c], Gl[c + 1], Gl[c + 2], Gl[c + 3]};
-                }
-                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-                __builtin_amdgcn_wave_barrier();
-                {
-                    float2* e2 = reinterpret_cast<float2*>(&sm.etot[pw][(2 * l) & (DK - 1)]);
-                    float2 x = *e2;
-                    x.x = fast_exp2(x.x);
-                    x.y = fast_exp2(x.y);
-                    __builtin_amdgcn_wave_barrier();
-                    if (2 * l < DK) {
-                        *e2 = x;
-                        *reinterpret_cast<hx2*>(&sm.etoth[pw][2 * l]) = __builtin_convertvector(f2{x.x, x.y}, hx2);
-                    }
-                }
                 // gates, beta and v are used up
                 asm volatile("" ::: "memory");
                 if (more) load_gbv(cm + kChunk);
@@ -573,10 +555,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 const float rkb = rkk * beta;
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk) {
+                    float rh[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int c = 8 * kk + j;
                         const float rho = fast_exp2(Gl[c]), iota = fast_exp2(-Gl[c]);
+                        rh[j] = rho;
                         Rq[kk][j] = (h16)(rq[c] * (rqs * rho));
                         Rk[kk][j] = (h16)(rk[c] * (rkb * rho));
                         Cd[kk][j] = (h16)(rk[c] * (rkk * iota));
@@ -587,6 +571,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                     // later blocks read this block's column operands
                     if constexpr (pw < 3)
                         *reinterpret_cast<h8*>(&sm.kcol[pw][cl * PK + CPL * qg + 8 * kk]) = Cd[kk];
+                    // the block's last row holds 2^(block total) per channel (fp32 and
+                    // fp16), which phase B reads for the other blocks' decays
+                    if (cl == 15) {
+                        float* et = &sm.etot[pw][CPL * qg + 8 * kk];
+                        *reinterpret_cast<f32x4*>(et) = f32x4{rh[0], rh[1], rh[2], rh[3]};
+                        *reinterpret_cast<f32x4*>(et + 4) = f32x4{rh[4], rh[5], rh[6], rh[7]};
+                        h8 eh;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) eh[j] = (h16)rh[j];
+                        *reinterpret_cast<h8*>(&sm.etoth[pw][CPL * qg + 8 * kk]) = eh;
+                    }
                 }
                 // q and k are used up
                 asm volatile("" ::: "memory");
@@ -602,8 +597,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 // state wave pw forms in phase B (it has the time there)
                 sm.ninv[pw][l] = __builtin_shufflevector(cvt4(d1), cvt4(d2), 0, 1, 2, 3, 4, 5, 6, 7);
                 if (SAVE && slice == 0 && qg == 0 && rr < Lm) {
-                    p.nq_saved[(cm + rr) * H + h] = nq;
-                    p.nk_saved[(cm + rr) * H + h] = nk;
+                    p.nq_saved[(cm + rr) * H + h] = sqrtf(ssq);
+                    p.nk_saved[(cm + rr) * H + h] = sqrtf(ssk);
                 }
             }
             lds_barrier();
