@@ -633,24 +633,33 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         RawRow<T, CPH> q[4], k[4];
         float G[4][CPH], GC[CPH], beta[4], iq[4], ik[4], lg[4];   // lg: the beta logits
     };
-    // after_loads runs once the row loads are issued, before their first use:
-    // more loads issued there wait only behind these
-    auto prep_fill = [&](Prep& P, bool first, auto after_loads) {
-        RawRow<T, CPH> rg[4];
+    // the lane's raw rows as loaded (prep_load issues the loads, prep_finish
+    // first uses them), so that a later step can have its rows in flight early
+    struct PrepRaw {
+        RawRow<T, CPH> q[4], k[4], g[4];
         float rb[4], nq[4], nk[4];
+    };
+    auto prep_load = [&](PrepRaw& R) {
         // rows past the chunk end load the last row (in bounds) and are zeroed
-        // below, once every load of the chunk is in flight
+        // in prep_finish, once every load of the chunk is in flight
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rc = min(r0 + i, L - 1);
-            P.q[i].load(qc + (rc * rk32 + ck0));
-            P.k[i].load(kc + (rc * rk32 + ck0));
-            rg[i].load(gcp + (rc * rk32 + ck0));
-            rb[i] = gload1(bc + rc * H);
-            nq[i] = nqc[rc * H];     // norms saved by the forward
-            nk[i] = nkc[rc * H];
+            R.q[i].load(qc + (rc * rk32 + ck0));
+            R.k[i].load(kc + (rc * rk32 + ck0));
+            R.g[i].load(gcp + (rc * rk32 + ck0));
+            R.rb[i] = gload1(bc + rc * H);
+            R.nq[i] = nqc[rc * H];     // norms saved by the forward
+            R.nk[i] = nkc[rc * H];
         }
-        after_loads();
+    };
+    auto prep_finish = [&](Prep& P, PrepRaw& R, bool first) {
+        RawRow<T, CPH>* rg = R.g;
+        const float* rb = R.rb;
+        const float* nq = R.nq;
+        const float* nk = R.nk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { P.q[i] = R.q[i]; P.k[i] = R.k[i]; }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool ok = r0 + i < L;
@@ -692,6 +701,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             for (int i = 0; i < 4; ++i) P.G[i][e] += a;
             P.GC[e] = tot;
         }
+    };
+    // after_loads runs once the row loads are issued, before their first use:
+    // more loads issued there wait only behind these
+    auto prep_fill = [&](Prep& P, bool first, auto after_loads) {
+        PrepRaw R;
+        prep_load(R);
+        after_loads();
+        prep_finish(P, R, first);
     };
     // prep-layout value of qh*Gam, beta*kh*Gam, kh/Gam at (row i, col e)
     auto vQG = [&](const Prep& P, int i, int e) { return P.q[i][e] * P.iq[i] * fast_exp2(P.G[i][e]); };
@@ -1151,6 +1168,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     lds_barrier();
 
     // ================= back to the prep layout (fp32 through LDS) =================
+    // (the chain rule's rows go out now and arrive during the transposes)
+    PrepRaw R3;
+    prep_load(R3);
     constexpr int LDF = DK + 4;
     float* const F0 = Sf(0);   // slots 0-1
     float* const F1 = Sf(2);   // slots 2-3
@@ -1188,7 +1208,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 
     // ================= chain rule to qh, kh, beta, G =================
     Prep P;
-    prep_fill(P, false, [] {});
+    prep_finish(P, R3, false);
     float dqh[4][CPH], dkh[4][CPH], dG[4][CPH], dbk[4], colp[CPH];
 #pragma unroll
     for (int e = 0; e < CPH; ++e) colp[e] = 0.f;
