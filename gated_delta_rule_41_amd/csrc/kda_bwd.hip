@@ -1175,6 +1175,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     float* const F0 = Sf(0);   // slots 0-1
     float* const F1 = Sf(2);   // slots 2-3
     float* const F2 = Sf(4);   // slots 4-5
+    float* const F3 = Sf(6);   // slots 6-7
     static_assert(kChunk * LDF * 4 <= 2 * LY::SLOT, "fp32 staging");
     float gQ[4][CPH], gKG[4][CPH], gKI[4][CPH], gKt[4][CPH];
     if (kact) {
@@ -1183,6 +1184,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             st_blk(F0, LDF, 16 * mb, 16 * w, dQG[mb], qg, cl);
             st_blk(F1, LDF, 16 * mb, 16 * w, dKG[mb], qg, cl);
             st_blk(F2, LDF, 16 * mb, 16 * w, dKI[mb], qg, cl);
+            st_blk(F3, LDF, 16 * mb, 16 * w, dKt[mb], qg, cl);
         }
     }
     lds_barrier();
@@ -1194,17 +1196,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             gQ[i][e] = F0[o];
             gKG[i][e] = F1[o];
             gKI[i][e] = F2[o];
+            gKt[i][e] = F3[o];
         }
-    lds_barrier();
-    if (kact) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) st_blk(F0, LDF, 16 * mb, 16 * w, dKt[mb], qg, cl);
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < CPH; ++e) gKt[i][e] = F0[(r0 + i) * LDF + ck0 + e];
 
     // ================= chain rule to qh, kh, beta, G =================
     Prep P;
