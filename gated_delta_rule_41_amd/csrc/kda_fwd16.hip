@@ -684,21 +684,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         if (!MAP) aoff[jb][1] = mma32(aoff[jb][1], a, Rq[kk]);
                         f = f * E[jb];
                     }
-                    if constexpr (pw == 0) {
-                        if (cl == 0) {
-                            // 2^G_C in fp32 (it scales the fp32 state)
-#pragma unroll
-                            for (int hf = 0; hf < 2; ++hf) {
-                                f32x4 gc = *reinterpret_cast<const f32x4*>(&sm.etot[0][CPL * qg + 8 * kk + 4 * hf]);
-#pragma unroll
-                                for (int b = 1; b < 4; ++b)
-                                    gc *= *reinterpret_cast<const f32x4*>(&sm.etot[b][CPL * qg + 8 * kk + 4 * hf]);
-                                *reinterpret_cast<f32x4*>(&B.gamc[CPL * qg + 8 * kk + 4 * hf]) = gc;
-                            }
-                        }
-                    }
-                    // keep the next group's LDS reads behind this group's work
                     asm volatile("" ::: "memory");
+                }
+                if constexpr (pw == 0) {
+                    // 2^G_C in fp32 (it scales the fp32 state): two channels per lane
+                    if (2 * l < DK) {
+                        float2 gc = *reinterpret_cast<const float2*>(&sm.etot[0][2 * l]);
+#pragma unroll
+                        for (int b = 1; b < 4; ++b) {
+                            const float2 x = *reinterpret_cast<const float2*>(&sm.etot[b][2 * l]);
+                            gc.x *= x.x;
+                            gc.y *= x.y;
+                        }
+                        *reinterpret_cast<float2*>(&B.gamc[2 * l]) = gc;
+                    }
                 }
 #pragma unroll
                 for (int jb = 0; jb < pw; ++jb) {
