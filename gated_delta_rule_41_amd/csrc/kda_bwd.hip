@@ -426,6 +426,27 @@ __device__ __forceinline__ void st_blk(float* M, int ld, int m0, int n0, f32x4 x
 }
 
 
+// Sixteen sums over the 16 lanes of each row group, one per lane: at each
+// halving step a lane keeps the half of the remaining sums that its lane bit
+// selects and adds its partner's copy of that half (the partner differs in that
+// bit), so lane cl ends with the sum of v[cl].  v is used as scratch.
+__device__ __forceinline__ float row16_scatter(float (&v)[16], int cl) {
+    auto halve = [&](auto half, auto ctrl, int bit) {
+        constexpr int hh = decltype(half)::value;
+#pragma unroll
+        for (int j = 0; j < hh; ++j) {
+            const float keep = bit ? v[j + hh] : v[j];
+            const float send = bit ? v[j] : v[j + hh];
+            v[j] = keep + dpp<decltype(ctrl)::value>(send);
+        }
+    };
+    halve(std::integral_constant<int, 8>{}, std::integral_constant<int, 0x140>{}, (cl >> 3) & 1);   // row_mirror
+    halve(std::integral_constant<int, 4>{}, std::integral_constant<int, 0x141>{}, (cl >> 2) & 1);   // row_half_mirror
+    halve(std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{}, (cl >> 1) & 1);    // quad_perm [2,3,0,1]
+    halve(std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{}, cl & 1);           // quad_perm [1,0,3,2]
+    return v[0];
+}
+
 // Slot layout of the chunk kernel's LDS (bytes).
 template <typename T, int DK, int DV>
 struct ChunkLds {
@@ -965,14 +986,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             }
         }
         // waves 0-3 write their row sums; waves 4-7 park theirs in sred (unused
-        // until the chain rule) and add them after the next barrier
+        // until the chain rule) and add them after the next barrier; lane cl
+        // holds the sum of rows 16(cl>>2) + 4qg + (cl&3)
+        float v[16];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float s = row16_sum(rowpart[mb][i]);
-                if (cl == 0) (w < 4 ? sdbv : sred)[(w & 3) * 64 + 16 * mb + 4 * qg + i] = s;
-            }
+        for (int j = 0; j < 16; ++j) v[j] = rowpart[j >> 2][j & 3];
+        (w < 4 ? sdbv : sred)[(w & 3) * 64 + 16 * (cl >> 2) + 4 * qg + (cl & 3)] = row16_scatter(v, cl);
     }
     // ================= dAqk = lower(dO U^T);  dT = (dU v^T) diag(beta) (waves 0-3) =================
     f32x4 dAqk[4], dT[4];
@@ -1234,19 +1253,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     }
     // per-half row sums: qh . dqh, kh . dkh, and the k part of dbeta
     float* const srow = F0;   // [2 halves][3][64]
+    {
+        // v[4 kind + i]: kind 0 qh . dqh, 1 kh . dkh, 2 dbeta (k part) of row r0 + i
+        float v[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float sq = 0.f, sk = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int e = 0; e < CPH; ++e) { sq += P.q[i][e] * P.iq[i] * dqh[i][e]; sk += P.k[i][e] * P.ik[i] * dkh[i][e]; }
-        sq = row16_sum(sq);
-        sk = row16_sum(sk);
-        const float db = row16_sum(dbk[i]);
-        if (cl == 0) {
-            srow[(wh * 3 + 0) * 64 + r0 + i] = sq;
-            srow[(wh * 3 + 1) * 64 + r0 + i] = sk;
-            srow[(wh * 3 + 2) * 64 + r0 + i] = db;
+            for (int e = 0; e < CPH; ++e) { sq += P.q[i][e] * P.iq[i] * dqh[i][e]; sk += P.k[i][e] * P.ik[i] * dkh[i][e]; }
+            v[i] = sq;
+            v[4 + i] = sk;
+            v[8 + i] = dbk[i];
+            v[12 + i] = 0.f;
         }
+        const float t = row16_scatter(v, cl);
+        if (cl < 12) srow[(wh * 3 + (cl >> 2)) * 64 + r0 + (cl & 3)] = t;
     }
     lds_barrier();
     FC dGC = *reinterpret_cast<const FC*>(&spart[ck0]);
