@@ -241,7 +241,7 @@ kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q
             e = kda::launch_fwd_maps(pm, cfg->dk, st);
         }
         if (e == hipSuccess) {   // the state entering every segment
-            kda::CarryParams cp = {doc_seg, s0, maps, s_in, N, cfg->H, cfg->dv, cfg->dv / kda::kSlice};
+            kda::CarryParams cp = {doc_seg, s0, maps, s_in, N, cfg->H, cfg->dv, cfg->dv / kda::kCarryCols};
             e = kda::launch_carry(cp, cfg->dk, st);
         }
         if (e == hipSuccess) {   // the segments from their entering states

@@ -9,6 +9,7 @@ namespace kda {
 
 constexpr int kChunk = 64;      // tokens per chunk
 constexpr int kSlice = 64;      // value columns per forward / reverse-scan workgroup
+constexpr int kCarryCols = 16;  // value columns per segment-carry workgroup
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kWideThreads = 512;   // 8 wave64: four state waves + four prep waves (bf16 kernels)
 
@@ -90,7 +91,7 @@ struct CarryParams {
     const float* s0;     // [N,H,dk,dv] or nullptr
     const float* maps;   // [P,H,dk,dk+dv]: [M | B] of every segment
     float* s_in;         // [P,H,dk,dv]: the state entering every segment
-    int32_t N, H, dv, nslices;
+    int32_t N, H, dv, nslices;   // nslices = dv / kCarryCols
 };
 
 struct BwdParams {

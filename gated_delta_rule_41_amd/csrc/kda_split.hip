@@ -88,23 +88,25 @@ hipError_t launch_segments(const SegParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// One workgroup per (document, head, 64-wide value slice): walks the
+// One workgroup per (document, head, 16-wide value slice): walks the
 // document's segments in order, writing the state entering each and applying
-// S <- M S + B.  The slice of S (dk x 64) and M (dk x dk) sit in LDS; thread
-// (r, c) computes row r = tid / TPR, columns c*CPT .. c*CPT + CPT - 1.
+// S <- M S + B.  The slice of S (dk x 16) and M (dk x dk) sit in LDS; thread
+// (r, c) computes row r = tid / TPR, columns c*CPT .. c*CPT + CPT - 1.  Narrow
+// slices put dv/16 workgroups on every (document, head), so that the few
+// sequential chains of a long-context call spread over more compute units.
 template <int DK>
 __global__ __launch_bounds__(kThreads) void kda_carry_kernel(CarryParams p) {
     constexpr int TPR = kThreads / DK;     // threads per state row (2 or 4)
-    constexpr int CPT = kSlice / TPR;      // columns per thread (32 or 16)
-    constexpr int PM = DK + 4;             // padded row stride of M in LDS
-    __shared__ float sS[DK][kSlice];
-    __shared__ float sM[DK][PM];
+    constexpr int CPT = kCarryCols / TPR;  // columns per thread (8 or 4)
+    constexpr int PM = DK + 4;             // padded row stride of M in LDS (16-byte rows)
+    __shared__ float sS[DK][kCarryCols];
+    __shared__ __attribute__((aligned(16))) float sM[DK][PM];
     const int tid = threadIdx.x;
     const int nh = blockIdx.x / p.nslices, slice = blockIdx.x % p.nslices;
     const int n = nh / p.H, h = nh % p.H;
     const int dv = p.dv, ldm = DK + dv;
     const int r = tid / TPR, c0 = (tid % TPR) * CPT;
-    const int col = slice * kSlice + c0;    // value column of the thread's first output
+    const int col = slice * kCarryCols + c0;    // value column of the thread's first output
     const int j0 = p.doc_seg[n], j1 = p.doc_seg[n + 1];
 
     float x[CPT];
@@ -121,8 +123,7 @@ __global__ __launch_bounds__(kThreads) void kda_carry_kernel(CarryParams p) {
         for (int c = 0; c < CPT; ++c) sS[r][c0 + c] = x[c];
         for (int e = tid; e < DK * DK / 4; e += kThreads) {
             const int rr = e / (DK / 4), cc = 4 * (e % (DK / 4));
-            const f32x4 m = *reinterpret_cast<const f32x4*>(mp + (int64_t)rr * ldm + cc);
-            sM[rr][cc] = m[0]; sM[rr][cc + 1] = m[1]; sM[rr][cc + 2] = m[2]; sM[rr][cc + 3] = m[3];
+            *reinterpret_cast<f32x4*>(&sM[rr][cc]) = *reinterpret_cast<const f32x4*>(mp + (int64_t)rr * ldm + cc);
         }
         const float* bp = mp + (int64_t)r * ldm + DK + col;
 #pragma unroll
