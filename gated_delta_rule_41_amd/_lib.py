@@ -18,6 +18,9 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SAVE_FOR_BWD = 1
 KDA_FLAG_SEQUENTIAL = 2
+KDA_FLAG_STAGED = 4
+# kda_stage (include/kda.h), in order
+STAGES = ("G", "Akk", "Aqk", "T", "W", "Ut", "U", "S_in", "QG", "Ktil", "GamC")
 
 
 class KdaConfig(ctypes.Structure):
@@ -71,6 +74,8 @@ def load():
     cfgp = ctypes.POINTER(KdaConfig)
     lib.kda_config_init.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.kda_config_init.restype = None
+    lib.kda_stage_offset.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.kda_stage_offset.restype = ctypes.c_size_t
     for name in ("kda_saved_size", "kda_fwd_workspace_size", "kda_bwd_workspace_size"):
         fn = getattr(lib, name)
         fn.argtypes = [cfgp, ctypes.c_int64, ctypes.c_int32]
@@ -117,6 +122,10 @@ def kda_saved_size(cfg: KdaConfig, total_tokens: int, num_seqs: int) -> int:
 
 def kda_fwd_workspace_size(cfg: KdaConfig, total_tokens: int, num_seqs: int) -> int:
     return int(load().kda_fwd_workspace_size(ctypes.byref(cfg), total_tokens, num_seqs))
+
+
+def kda_stage_offset(cfg: KdaConfig, total_tokens: int, num_seqs: int, stage: int) -> int:
+    return int(load().kda_stage_offset(ctypes.byref(cfg), total_tokens, num_seqs, stage))
 
 
 def kda_bwd_workspace_size(cfg: KdaConfig, total_tokens: int, num_seqs: int) -> int:

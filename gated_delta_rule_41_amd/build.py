@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_fwd.hip", "kda_fwd16.hip", "kda_bwd.hip", "kda_decode.hip", "kda_split.hip", "kda_exact.hip", "kda_scan16.hip"]
+SOURCES = ["kda_api.hip", "kda_fwd.hip", "kda_fwd16.hip", "kda_bwd.hip", "kda_decode.hip", "kda_split.hip", "kda_exact.hip", "kda_scan16.hip",
+           "kda_staged.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -58,7 +58,8 @@ kda_status check_config_common(const kda_config* c) {
         return fail(KDA_ERR_INVALID_ARG, "unknown dtype%s");
     if (!(c->l2_eps >= 0.f) || !isfinite(c->l2_eps)) return fail(KDA_ERR_INVALID_ARG, "l2_eps must be finite and >= 0%s");
     if (!isfinite(c->scale)) return fail(KDA_ERR_INVALID_ARG, "scale must be finite%s");
-    if (c->flags & ~(KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL)) return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
+    if (c->flags & ~(KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL | KDA_FLAG_STAGED))
+        return fail(KDA_ERR_INVALID_ARG, "unknown flag bits%s");
     return KDA_OK;
 }
 
@@ -138,7 +139,8 @@ struct SplitPlan {
 SplitPlan split_plan(const kda_config* c, int64_t T, int32_t N) {
     SplitPlan s;
     memset(&s, 0, sizeof s);
-    if (c->in_dtype != KDA_BF16 || (c->flags & (KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL)) || N < 1 || T < 1)
+    if (c->in_dtype != KDA_BF16 || (c->flags & (KDA_FLAG_SAVE_FOR_BWD | KDA_FLAG_SEQUENTIAL | KDA_FLAG_STAGED)) ||
+        N < 1 || T < 1)
         return s;
     const int64_t chains = (int64_t)N * c->H * (c->dv / kda::kSlice);
     if (chains >= kSplitMaxChains) return s;
@@ -172,6 +174,26 @@ size_t bwd_flag_bytes(const kda_config* c, int64_t T, int32_t N) {
     return align256((size_t)kda::num_slots(T, N) * c->H * sizeof(int32_t));
 }
 
+// The staged forward's workspace: the eleven fp32 stage buffers of
+// kda_stage, each [slots, H, ...] and 256-byte aligned, in enum order.
+size_t stage_bytes(const kda_config* c, int64_t T, int32_t N, int stage) {
+    const size_t sh = (size_t)kda::num_slots(T, N) * c->H * sizeof(float);
+    const size_t C = kda::kChunk, dk = c->dk, dv = c->dv;
+    switch (stage) {
+        case KDA_STAGE_G: case KDA_STAGE_W: case KDA_STAGE_QG: case KDA_STAGE_KTIL: return align256(sh * C * dk);
+        case KDA_STAGE_AKK: case KDA_STAGE_AQK: case KDA_STAGE_T: return align256(sh * C * C);
+        case KDA_STAGE_UT: case KDA_STAGE_U: return align256(sh * C * dv);
+        case KDA_STAGE_S_IN: return align256(sh * dk * dv);
+        case KDA_STAGE_GAMC: return align256(sh * dk);
+        default: return 0;
+    }
+}
+size_t stage_offset(const kda_config* c, int64_t T, int32_t N, int stage) {
+    size_t off = 0;
+    for (int i = 0; i < stage; ++i) off += stage_bytes(c, T, N, i);
+    return off;
+}
+
 // Every argument check of kda_fwd except the workspace's.
 kda_status fwd_check(const kda_config* cfg, int64_t T, int32_t N, const void* q, const void* k, const void* v,
                      const void* g, const void* beta, const int32_t* cu, const float* s0, const void* o,
@@ -189,6 +211,8 @@ kda_status fwd_check(const kda_config* cfg, int64_t T, int32_t N, const void* q,
     KDA_TRY_(opt_ptr(cu, "cu_seqlens"));
     KDA_TRY_(opt_ptr(s0, "initial_state"));
     KDA_TRY_(opt_ptr(sfinal, "final_state"));
+    if ((cfg->flags & KDA_FLAG_STAGED) && (cfg->flags & KDA_FLAG_SAVE_FOR_BWD))
+        return fail(KDA_ERR_UNSUPPORTED, "KDA_FLAG_STAGED does not fill the saved buffer%s");
     if (cfg->flags & KDA_FLAG_SAVE_FOR_BWD) {
         KDA_TRY_(need_ptr(saved, "saved"));
         if (saved_bytes < kda_saved_size(cfg, T, N)) return fail(KDA_ERR_WORKSPACE, "saved buffer too small%s");
@@ -221,7 +245,19 @@ kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q
     p.nslices = cfg->dv / kda::kSlice;
     const SplitPlan sp = split_plan(cfg, T, N);
     hipError_t e = hipSuccess;
-    if (!sp.on) {
+    if (cfg->flags & KDA_FLAG_STAGED) {
+        kda::StagedParams sp2;
+        memset(&sp2, 0, sizeof sp2);
+        sp2.q = q; sp2.k = k; sp2.v = v; sp2.g = g; sp2.b = beta;
+        sp2.cu = cu; sp2.s0 = s0; sp2.o = o; sp2.sfinal = sfinal;
+        float** dst[KDA_STAGE_COUNT] = {&sp2.G, &sp2.Akk, &sp2.Aqk, &sp2.Tm, &sp2.W, &sp2.Ut,
+                                        &sp2.U, &sp2.Sin, &sp2.QG, &sp2.Ktil, &sp2.GamC};
+        for (int i = 0; i < KDA_STAGE_COUNT; ++i) *dst[i] = (float*)((char*)workspace + stage_offset(cfg, T, N, i));
+        sp2.T = T; sp2.N = N; sp2.H = cfg->H; sp2.dv = cfg->dv;
+        sp2.seqlen = p.seqlen;
+        sp2.eps = cfg->l2_eps; sp2.scale = cfg->scale;
+        if (T > 0) e = kda::launch_fwd_staged(sp2, cfg->in_dtype, cfg->out_dtype, cfg->dk, st);
+    } else if (!sp.on) {
         e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, st);
     } else {
         char* ws = (char*)workspace;
@@ -315,7 +351,13 @@ size_t kda_saved_size(const kda_config* cfg, int64_t T, int32_t N) {
 
 size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {
     if (check_config(cfg) != KDA_OK || T < 0 || N < 1) return 0;
+    if (cfg->flags & KDA_FLAG_STAGED) return stage_offset(cfg, T, N, KDA_STAGE_COUNT);
     return split_plan(cfg, T, N).total;
+}
+
+size_t kda_stage_offset(const kda_config* cfg, int64_t T, int32_t N, int32_t stage) {
+    if (check_config(cfg) != KDA_OK || T < 0 || N < 1 || stage < 0 || stage > KDA_STAGE_COUNT) return 0;
+    return stage_offset(cfg, T, N, stage);
 }
 
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t T, int32_t N) {

@@ -88,6 +88,8 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* kda_config.flags */
 #define KDA_FLAG_SAVE_FOR_BWD 1u /* forward also fills `saved` for kda_bwd */
 #define KDA_FLAG_SEQUENTIAL 2u   /* forward: never split long sequences into segments */
+#define KDA_FLAG_STAGED 4u       /* forward: the staged correctness path, every stage
+                                    written to the workspace (see kda_stage) */
 
 typedef struct kda_config {
     int32_t H;         /* heads                                        */
@@ -106,15 +108,58 @@ void kda_config_init(kda_config* cfg, int32_t H, int32_t dk, int32_t dv);
 
 /* Sizes in bytes (pure host functions; 0 for an invalid config).
  * kda_saved_size: the buffer kda_fwd fills under KDA_FLAG_SAVE_FOR_BWD and
- * kda_bwd reads: per-chunk entering states (fp32), the per-token q/k norms
- * and, for bf16 inputs, each chunk's pseudo-values U = T beta v - W S (fp32).
+ * kda_bwd reads: per-chunk entering states, the per-token q/k norms (fp32)
+ * and, for bf16 inputs, each chunk's pseudo-values U = T beta v - W S; for
+ * bf16 inputs the states and U are fp16, each (chunk, head, 16 value columns)
+ * scaled by a power of two kept beside them in fp32, for fp32 inputs the
+ * states are fp32.
  * kda_fwd_workspace_size / kda_bwd_workspace_size: scratch for one call (the
  * backward's holds dL/dS at the end of every chunk and, for bf16 inputs, each
- * chunk's dL/dU; the forward's is non-zero only when it splits long sequences,
- * see kda_fwd). */
+ * chunk's dL/dU, stored like the saved states; the forward's is non-zero only
+ * when it splits long sequences, see kda_fwd, or under KDA_FLAG_STAGED, where
+ * it holds the stages of kda_stage). */
 size_t kda_saved_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_fwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
 size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs);
+
+/* The staged forward (KDA_FLAG_STAGED on kda_fwd).  The chunk form of the
+ * pages' intra-chunk processing plus inter-chunk state passing ("TorchTitan
+ * Ascend open source: Kimi K3.1 Pro adaptation and training practice", section
+ * "KDA pre/post-processing fusion"), run as two launches that write every
+ * intermediate to the workspace: first every chunk in parallel (G, Akk, Aqk,
+ * T, W, Ut and the scan's operands), then the state pass per document (U, o,
+ * the entering states).  Plain fp32 arithmetic with the decay of every token
+ * pair formed directly, so any g <= 0; slow; meant as a cross-check of the
+ * fused kernels, stage by stage.  o and final_state are as from kda_fwd.
+ * KDA_FLAG_SAVE_FOR_BWD with it returns KDA_ERR_UNSUPPORTED; the other entry
+ * points ignore the flag.
+ *
+ * Each stage is an fp32 array indexed [slot][head][...], where chunk j of
+ * document n (tokens cu[n] + 64 j ..) has slot floor(cu[n] / 64) + n + j; a
+ * chunk's rows (and Akk/Aqk/T columns) past its document's end are zero, and
+ * slots no chunk maps to are left unwritten.  With G the in-chunk inclusive
+ * cumsum of g, qh, kh the normalised q (times scale) and k, E_rs =
+ * exp(G_r - G_s) per channel: */
+typedef enum kda_stage {
+    KDA_STAGE_G = 0,    /* [64][dk] G                                              */
+    KDA_STAGE_AKK = 1,  /* [64][64] beta_r sum_c kh_r kh_s E_rs for s < r, else 0  */
+    KDA_STAGE_AQK = 2,  /* [64][64] sum_c qh_r kh_s E_rs for s <= r, else 0        */
+    KDA_STAGE_T = 3,    /* [64][64] (I + Akk)^-1                                   */
+    KDA_STAGE_W = 4,    /* [64][dk] T (beta kh exp(G))                             */
+    KDA_STAGE_UT = 5,   /* [64][dv] T (beta v)                                     */
+    KDA_STAGE_U = 6,    /* [64][dv] Ut - W S_in                                    */
+    KDA_STAGE_S_IN = 7, /* [dk][dv] the state entering the chunk                   */
+    KDA_STAGE_QG = 8,   /* [64][dk] qh exp(G)                                      */
+    KDA_STAGE_KTIL = 9, /* [64][dk] kh exp(G_C - G), G_C = G of the chunk's last row */
+    KDA_STAGE_GAMC = 10, /* [dk]    exp(G_C)                                       */
+    KDA_STAGE_COUNT = 11
+} kda_stage;
+
+/* Byte offset of `stage` in the workspace of a KDA_FLAG_STAGED forward
+ * (stage = KDA_STAGE_COUNT gives the total, which equals
+ * kda_fwd_workspace_size under the flag).  Pure host function; 0 for an
+ * invalid config or stage. */
+size_t kda_stage_offset(const kda_config* cfg, int64_t total_tokens, int32_t num_seqs, int32_t stage);
 
 /* Forward.  o: [total_tokens, H, dv] in out_dtype.  initial_state: fp32
  * [num_seqs, H, dk, dv] or NULL (zero state; every document starts from its

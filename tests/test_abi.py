@@ -190,8 +190,34 @@ def test_fwd_workspace_for_long_sequences():
     assert _fwd(long_cfg, T=1 << 20, ws=FAKE, wsb=ws - 1) == KDA_ERR_WORKSPACE
     assert _fwd(long_cfg, T=1 << 20, ws=0, wsb=ws) == KDA_ERR_INVALID_ARG and "workspace" in _err()
     cfg = _lib.make_config(2, 64, 64, KDA_BF16)
-    cfg.flags = 4
+    cfg.flags = 8
     assert _fwd(cfg) == KDA_ERR_INVALID_ARG
+
+
+def test_staged_forward_workspace_and_checks():
+    """KDA_FLAG_STAGED: the workspace holds the eleven fp32 stages of kda_stage,
+    each [slots, H, ...], 256-byte aligned, in enum order; the flag excludes the
+    state save; a short or missing workspace is refused before any launch."""
+    T, N, H, dk, dv = 247, 3, 2, 128, 64
+    cfg = _lib.make_config(H, dk, dv, KDA_BF16, KDA_F32, flags=_lib.KDA_FLAG_STAGED)
+    slots = T // 64 + N
+    tails = {"G": 64 * dk, "Akk": 64 * 64, "Aqk": 64 * 64, "T": 64 * 64, "W": 64 * dk, "Ut": 64 * dv,
+             "U": 64 * dv, "S_in": dk * dv, "QG": 64 * dk, "Ktil": 64 * dk, "GamC": dk}
+    off = [_lib.kda_stage_offset(cfg, T, N, i) for i in range(len(_lib.STAGES) + 1)]
+    assert off[0] == 0
+    for i, name in enumerate(_lib.STAGES):
+        size = slots * H * tails[name] * 4
+        assert off[i] % 256 == 0 and off[i + 1] - off[i] == (size + 255) // 256 * 256, name
+    need = _lib.kda_fwd_workspace_size(cfg, T, N)
+    assert need == off[-1] > 0
+    assert _lib.kda_stage_offset(cfg, T, N, len(_lib.STAGES) + 1) == 0
+    assert _lib.kda_stage_offset(cfg, T, N, -1) == 0
+    assert _fwd(cfg, T=T, N=N, cu=FAKE, ws=FAKE, wsb=need - 1) == KDA_ERR_WORKSPACE
+    assert _fwd(cfg, T=T, N=N, cu=FAKE, ws=0, wsb=need) == KDA_ERR_INVALID_ARG and "workspace" in _err()
+    both = _lib.make_config(H, dk, dv, KDA_BF16, KDA_F32, flags=_lib.KDA_FLAG_STAGED | KDA_FLAG_SAVE_FOR_BWD)
+    need_s = _lib.kda_saved_size(both, T, N)
+    assert _fwd(both, T=T, N=N, cu=FAKE, saved=FAKE, saved_bytes=need_s, ws=FAKE, wsb=need) == KDA_ERR_UNSUPPORTED
+    assert "STAGED" in _err()
 
 
 def test_head_count_bound():
