@@ -107,17 +107,19 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: 
 
 
 def kda_fwd_staged(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num_seqs: Optional[int] = None,
-                   out_dtype=None, eps: float = 1e-6, scale: float = 1.0):
+                   out_dtype=None, eps: float = 1e-6, scale: float = 1.0, chunk: int = 64):
     """The staged forward (kda_fwd with KDA_FLAG_STAGED): the correctness path.
     Returns ``(o, final_state, stages)``; ``stages`` maps each name of
     ``_lib.STAGES`` to an fp32 view of the workspace shaped
     ``[slots, H, ...]`` (see kda_stage in include/kda.h): chunk j of
-    document n is slot ``cu[n] // 64 + n + j``."""
+    document n is slot ``cu[n] // chunk + n + j``.  ``chunk`` may be 16, 32
+    or 64."""
     torch = _torch()
     T, H, dk, dv, N, dev, dt = _common(q, k, v, g, beta, cu_seqlens, num_seqs)
     out_dtype = out_dtype or torch.float32
     _check(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
     cfg = make_config(H, dk, dv, _dt_code(dt), _dt_code(out_dtype), eps, scale, _lib.KDA_FLAG_STAGED)
+    cfg.chunk = chunk
     o = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
     sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     wsb = kda_fwd_workspace_size(cfg, T, N)
@@ -126,9 +128,10 @@ def kda_fwd_staged(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, num
         stream = torch.cuda.current_stream(dev).cuda_stream
         _lib.check(_lib.kda_fwd_raw(cfg, T, N, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                     _ptr(initial_state), _ptr(o), _ptr(sf), 0, 0, _ptr(ws), wsb, stream))
-    slots = T // 64 + N
-    tail = {"G": (64, dk), "Akk": (64, 64), "Aqk": (64, 64), "T": (64, 64), "W": (64, dk), "Ut": (64, dv),
-            "U": (64, dv), "S_in": (dk, dv), "QG": (64, dk), "Ktil": (64, dk), "GamC": (dk,)}
+    slots = T // chunk + N
+    C = chunk
+    tail = {"G": (C, dk), "Akk": (C, C), "Aqk": (C, C), "T": (C, C), "W": (C, dk), "Ut": (C, dv),
+            "U": (C, dv), "S_in": (dk, dv), "QG": (C, dk), "Ktil": (C, dk), "GamC": (dk,)}
     stages = {}
     for i, name in enumerate(_lib.STAGES):
         off = _lib.kda_stage_offset(cfg, T, N, i)

@@ -52,7 +52,8 @@ kda_status check_config_common(const kda_config* c) {
     if (c->H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1%s");
     if ((c->dk != 64 && c->dk != 128) || (c->dv != 64 && c->dv != 128))
         return fail(KDA_ERR_UNSUPPORTED, "dk and dv must be 64 or 128%s");
-    if (c->chunk != kda::kChunk) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64%s");
+    if (c->chunk != kda::kChunk && !((c->flags & KDA_FLAG_STAGED) && (c->chunk == 16 || c->chunk == 32)))
+        return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (16 or 32 only with KDA_FLAG_STAGED)%s");
     if ((c->in_dtype != KDA_F32 && c->in_dtype != KDA_BF16) ||
         (c->out_dtype != KDA_F32 && c->out_dtype != KDA_BF16))
         return fail(KDA_ERR_INVALID_ARG, "unknown dtype%s");
@@ -78,7 +79,8 @@ kda_status check_sizes(const kda_config* c, int64_t T, int32_t N, const int32_t*
     if (!cu && (T % N) != 0)
         return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is NULL but total_tokens is not a multiple of num_seqs%s");
     if (!grid_fits((int64_t)N * c->H * (c->dv / kda::kSlice), kda::kWideThreads) ||
-        !grid_fits(kda::num_slots(T, N) * c->H, kda::kWideThreads))
+        !grid_fits(kda::num_slots(T, N) * c->H, kda::kWideThreads) ||
+        !grid_fits((T / c->chunk + N) * c->H, kda::kWideThreads))
         return fail(KDA_ERR_UNSUPPORTED, "num_seqs, H or total_tokens too large for one launch%s");
     // the kernels address a chunk's rows with 32-bit offsets from a 64-bit base
     if ((int64_t)kda::kChunk * c->H * (c->dk > c->dv ? c->dk : c->dv) >= ((int64_t)1 << 31))
@@ -175,10 +177,11 @@ size_t bwd_flag_bytes(const kda_config* c, int64_t T, int32_t N) {
 }
 
 // The staged forward's workspace: the eleven fp32 stage buffers of
-// kda_stage, each [slots, H, ...] and 256-byte aligned, in enum order.
+// kda_stage, each [slots, H, ...] (slots = T / chunk + N) and 256-byte
+// aligned, in enum order.
 size_t stage_bytes(const kda_config* c, int64_t T, int32_t N, int stage) {
-    const size_t sh = (size_t)kda::num_slots(T, N) * c->H * sizeof(float);
-    const size_t C = kda::kChunk, dk = c->dk, dv = c->dv;
+    const size_t C = c->chunk, dk = c->dk, dv = c->dv;
+    const size_t sh = (size_t)(T / c->chunk + N) * c->H * sizeof(float);   // chunk slots x heads
     switch (stage) {
         case KDA_STAGE_G: case KDA_STAGE_W: case KDA_STAGE_QG: case KDA_STAGE_KTIL: return align256(sh * C * dk);
         case KDA_STAGE_AKK: case KDA_STAGE_AQK: case KDA_STAGE_T: return align256(sh * C * C);
@@ -256,7 +259,7 @@ kda_status fwd_launch(const kda_config* cfg, int64_t T, int32_t N, const void* q
         sp2.T = T; sp2.N = N; sp2.H = cfg->H; sp2.dv = cfg->dv;
         sp2.seqlen = p.seqlen;
         sp2.eps = cfg->l2_eps; sp2.scale = cfg->scale;
-        if (T > 0) e = kda::launch_fwd_staged(sp2, cfg->in_dtype, cfg->out_dtype, cfg->dk, st);
+        if (T > 0) e = kda::launch_fwd_staged(sp2, cfg->in_dtype, cfg->out_dtype, cfg->dk, cfg->chunk, st);
     } else if (!sp.on) {
         e = kda::launch_fwd(p, cfg->in_dtype, cfg->out_dtype, cfg->dk, save, st);
     } else {
@@ -441,6 +444,7 @@ static kda_status bwd_call(int stages, const kda_config* cfg, int64_t T, int32_t
                            size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     KDA_TRY(check_config(cfg));
+    if (cfg->chunk != kda::kChunk) return fail(KDA_ERR_UNSUPPORTED, "the backward runs chunks of 64 only%s");
     KDA_TRY(check_sizes(cfg, T, N, cu));
     if (T > 0) {
         KDA_TRY(need_ptr(q, "q"));

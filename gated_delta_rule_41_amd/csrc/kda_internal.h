@@ -95,8 +95,8 @@ struct CarryParams {
 };
 
 // The staged forward (KDA_FLAG_STAGED): inputs as FwdParams, and the stage
-// buffers it writes, all fp32, indexed by (slot * H + head):
-//   G, W, QG, Ktil [., 64, dk]   Akk, Aqk, Tm [., 64, 64]   Ut, U [., 64, dv]
+// buffers it writes, all fp32, indexed by (slot * H + head), C the chunk:
+//   G, W, QG, Ktil [., C, dk]    Akk, Aqk, Tm [., C, C]      Ut, U [., C, dv]
 //   Sin [., dk, dv]              GamC [., dk]
 struct StagedParams {
     const void* q;
@@ -176,7 +176,7 @@ hipError_t launch_fwd16_maps(const FwdParams& p, int dk, hipStream_t stream);
 // bf16 inputs: the reverse state-gradient scan with fp16 matrix-core operands (kda_scan16.hip).
 hipError_t launch_scan16(const BwdParams& p, int dk, hipStream_t stream);
 hipError_t launch_carry(const CarryParams& p, int dk, hipStream_t stream);
-hipError_t launch_fwd_staged(const StagedParams& p, int in_dtype, int out_dtype, int dk, hipStream_t stream);
+hipError_t launch_fwd_staged(const StagedParams& p, int in_dtype, int out_dtype, int dk, int chunk, hipStream_t stream);
 // Kernels without the chunk-start gate factorisation (kda_exact.hip): the
 // forward and the reverse scan token by token, and the chunk gradients with
 // the decay of every token pair formed directly (only_unsafe: only chunks whose

@@ -6,8 +6,9 @@
 // passing that the pages describe ("TorchTitan Ascend open source: Kimi K3.1
 // Pro adaptation and training practice", section "KDA pre/post-processing
 // fusion"; "Ascend implements LoRA training of Kimi K3.1 Pro", section "KDA:
-// big fused forward and backward").  Per (document, head) and chunk of C = 64
-// rows (fewer at a document's end), with G the in-chunk inclusive cumsum of g
+// big fused forward and backward").  Per (document, head) and chunk of C rows
+// (C = 64, or 16 or 32 for chunk-size invariance checks; fewer rows at a
+// document's end), with G the in-chunk inclusive cumsum of g
 // and E_rs = exp(G_r - G_s) per channel (s <= r, so E <= 1 for g <= 0):
 //
 //   Akk[r,s] = beta_r sum_c kh_r kh_s E_rs (s < r)    Aqk[r,s] = sum_c qh_r kh_s E_rs (s <= r)
@@ -29,12 +30,25 @@
 namespace kda {
 namespace staged {
 
-constexpr int PR = 128 + 1;        // row stride of the [64][<= 128] fp32 tiles (odd: rows spread over banks)
-constexpr int PA = kChunk + 1;     // row stride of the [64][64] tiles
+constexpr int PR = 128 + 1;        // row stride of the [C][<= 128] fp32 tiles (odd: rows spread over banks)
 
-template <typename T, int DK>
+// The document that owns chunk slot `slot` for chunk length C (slots as in
+// the fused kernels: floor(start / C) + document + chunk index).
+__device__ __forceinline__ int owner(const int32_t* cu, int N, int seqlen, int64_t slot, int C) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int64_t start = cu ? (int64_t)cu[mid] : (int64_t)mid * seqlen;
+        if (start / C + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void kda_staged_intra_kernel(StagedParams p) {
-    constexpr int C = kChunk;
+    constexpr int PA = C + 1;          // row stride of the [C][C] tiles
+    constexpr int TPR = kThreads / C;  // threads per row for the norms (4, 8 or 16)
     __shared__ float bufG[C * PR];     // G
     __shared__ float bufK[C * PR];     // kh, later beta v
     __shared__ float bufQ[C * PR];     // qh, later beta kh exp(G)
@@ -45,13 +59,13 @@ __global__ __launch_bounds__(kThreads) void kda_staged_intra_kernel(StagedParams
     const int H = p.H, dv = p.dv;
     const int64_t slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
-    const int n = slot_owner(p.cu, p.N, p.seqlen, slot);
+    const int n = owner(p.cu, p.N, p.seqlen, slot, C);
     int64_t t0, t1;
     seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
-    const int64_t jc = slot - (t0 / kChunk + n);
-    const int64_t c0 = t0 + jc * kChunk;
+    const int64_t jc = slot - (t0 / C + n);
+    const int64_t c0 = t0 + jc * C;
     if (jc < 0 || c0 >= t1) return;   // unused slot (uniform across the workgroup)
-    const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
+    const int L = (int)((t1 - c0) < C ? (t1 - c0) : C);
     const int64_t rsk = (int64_t)H * DK, rsv = (int64_t)H * dv;
     const T* qc = reinterpret_cast<const T*>(p.q) + c0 * rsk + (int64_t)h * DK;
     const T* kc = reinterpret_cast<const T*>(p.k) + c0 * rsk + (int64_t)h * DK;
@@ -77,11 +91,11 @@ __global__ __launch_bounds__(kThreads) void kda_staged_intra_kernel(StagedParams
             bufG[r * PR + tid] = a;
         }
     }
-    // the L2 norms: four threads per row
+    // the L2 norms: TPR adjacent threads per row
     {
-        const int r = tid >> 2, part = tid & 3;
+        const int r = tid / TPR, part = tid % TPR;
         float sq = 0.f, sk = 0.f;
-        for (int c = part; c < DK; c += 4) {
+        for (int c = part; c < DK; c += TPR) {
             const float qv = r < L ? to_f32(qc[r * rsk + c]) : 0.f;
             const float kv = r < L ? to_f32(kc[r * rsk + c]) : 0.f;
             sq += qv * qv;
@@ -89,12 +103,13 @@ __global__ __launch_bounds__(kThreads) void kda_staged_intra_kernel(StagedParams
             bufQ[r * PR + c] = qv;
             bufK[r * PR + c] = kv;
         }
-        sq += __shfl_xor(sq, 1);
-        sq += __shfl_xor(sq, 2);
-        sk += __shfl_xor(sk, 1);
-        sk += __shfl_xor(sk, 2);
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) {
+            sq += __shfl_xor(sq, m);
+            sk += __shfl_xor(sk, m);
+        }
         const float iq = p.scale / sqrtf(sq + p.eps), ik = 1.f / sqrtf(sk + p.eps);
-        for (int c = part; c < DK; c += 4) {
+        for (int c = part; c < DK; c += TPR) {
             bufQ[r * PR + c] *= iq;
             bufK[r * PR + c] *= ik;
         }
@@ -168,9 +183,9 @@ __global__ __launch_bounds__(kThreads) void kda_staged_intra_kernel(StagedParams
     }
 }
 
-template <typename TO, int DK>
+template <typename TO, int DK, int C>
 __global__ __launch_bounds__(kThreads) void kda_staged_scan_kernel(StagedParams p) {
-    constexpr int C = kChunk, SW = kSlice, PS = SW + 1;
+    constexpr int SW = kSlice, PS = SW + 1;
     __shared__ float sS[DK * PS];   // this slice of the state [c][j]
     __shared__ float sU[C * PS];    // U of the chunk [r][j]
     const int tid = threadIdx.x;
@@ -180,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void kda_staged_scan_kernel(StagedParams 
     const int j0 = slice * SW;
     int64_t t0, t1;
     seq_bounds(p.cu, n, p.seqlen, p.T, t0, t1);
-    const int nch = (int)((t1 - t0 + kChunk - 1) / kChunk);
+    const int nch = (int)((t1 - t0 + C - 1) / C);
     const int64_t sb = ((int64_t)n * H + h) * DK * dv;
     for (int e = tid; e < DK * SW; e += kThreads) {
         const int c = e / SW, j = e % SW;
@@ -189,9 +204,9 @@ __global__ __launch_bounds__(kThreads) void kda_staged_scan_kernel(StagedParams 
     __syncthreads();
     TO* op = reinterpret_cast<TO*>(p.o);
     for (int ic = 0; ic < nch; ++ic) {
-        const int64_t c0 = t0 + (int64_t)ic * kChunk;
-        const int L = (int)((t1 - c0) < kChunk ? (t1 - c0) : kChunk);
-        const int64_t bi = (t0 / kChunk + n + ic) * H + h;
+        const int64_t c0 = t0 + (int64_t)ic * C;
+        const int L = (int)((t1 - c0) < C ? (t1 - c0) : C);
+        const int64_t bi = (t0 / C + n + ic) * H + h;
         const float* W = p.W + bi * C * DK;
         const float* QG = p.QG + bi * C * DK;
         const float* Kt = p.Ktil + bi * C * DK;
@@ -242,28 +257,34 @@ __global__ __launch_bounds__(kThreads) void kda_staged_scan_kernel(StagedParams 
     }
 }
 
-template <typename T, typename TO, int DK>
-hipError_t launch_typed(const StagedParams& p, int64_t slots, hipStream_t s) {
-    const int64_t intra = slots * p.H;
+template <typename T, typename TO, int DK, int C>
+hipError_t launch_c(const StagedParams& p, hipStream_t s) {
+    const int64_t intra = (p.T / C + p.N) * p.H;   // chunk slots x heads
     const int64_t scan = (int64_t)p.N * p.H * (p.dv / kSlice);
     if (intra > 0)
-        hipLaunchKernelGGL((kda_staged_intra_kernel<T, DK>), dim3((unsigned)intra), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((kda_staged_intra_kernel<T, DK, C>), dim3((unsigned)intra), dim3(kThreads), 0, s, p);
     if (scan > 0)
-        hipLaunchKernelGGL((kda_staged_scan_kernel<TO, DK>), dim3((unsigned)scan), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((kda_staged_scan_kernel<TO, DK, C>), dim3((unsigned)scan), dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+template <typename T, typename TO, int DK>
+hipError_t launch_typed(const StagedParams& p, int chunk, hipStream_t s) {
+    if (chunk == 16) return launch_c<T, TO, DK, 16>(p, s);
+    if (chunk == 32) return launch_c<T, TO, DK, 32>(p, s);
+    return launch_c<T, TO, DK, 64>(p, s);
 }
 
 }  // namespace staged
 
-hipError_t launch_fwd_staged(const StagedParams& p, int in_dtype, int out_dtype, int dk, hipStream_t s) {
-    const int64_t slots = num_slots(p.T, p.N);
+hipError_t launch_fwd_staged(const StagedParams& p, int in_dtype, int out_dtype, int dk, int chunk, hipStream_t s) {
     const bool bin = in_dtype != 0, bout = out_dtype != 0;
     if (dk == 128) {
-        if (bin) return bout ? staged::launch_typed<bf16, bf16, 128>(p, slots, s) : staged::launch_typed<bf16, float, 128>(p, slots, s);
-        return bout ? staged::launch_typed<float, bf16, 128>(p, slots, s) : staged::launch_typed<float, float, 128>(p, slots, s);
+        if (bin) return bout ? staged::launch_typed<bf16, bf16, 128>(p, chunk, s) : staged::launch_typed<bf16, float, 128>(p, chunk, s);
+        return bout ? staged::launch_typed<float, bf16, 128>(p, chunk, s) : staged::launch_typed<float, float, 128>(p, chunk, s);
     }
-    if (bin) return bout ? staged::launch_typed<bf16, bf16, 64>(p, slots, s) : staged::launch_typed<bf16, float, 64>(p, slots, s);
-    return bout ? staged::launch_typed<float, bf16, 64>(p, slots, s) : staged::launch_typed<float, float, 64>(p, slots, s);
+    if (bin) return bout ? staged::launch_typed<bf16, bf16, 64>(p, chunk, s) : staged::launch_typed<bf16, float, 64>(p, chunk, s);
+    return bout ? staged::launch_typed<float, bf16, 64>(p, chunk, s) : staged::launch_typed<float, float, 64>(p, chunk, s);
 }
 
 }  // namespace kda

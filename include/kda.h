@@ -49,7 +49,8 @@
  *    A malformed cu_seqlens (decreasing, or last entry != total_tokens) is
  *    undefined behaviour; the kernels clamp every document to
  *    [0, total_tokens) so it cannot address memory outside the buffers.
- *  - Supported: dk, dv in {64, 128}; chunk = 64; in_dtype, out_dtype in
+ *  - Supported: dk, dv in {64, 128}; chunk = 64 (16 and 32 as well for the
+ *    staged forward, KDA_FLAG_STAGED); in_dtype, out_dtype in
  *    {KDA_F32, KDA_BF16}; H >= 1 with 64 * H * max(dk, dv) < 2^31 (the
  *    kernels address a chunk's rows with 32-bit offsets); total_tokens < 2^31;
  *    one launch covers at most 2^32 - 1 work-items, so num_seqs * H * dv/64
@@ -95,7 +96,7 @@ typedef struct kda_config {
     int32_t H;         /* heads                                        */
     int32_t dk;        /* key / query head dim (64 or 128)             */
     int32_t dv;        /* value head dim (64 or 128)                   */
-    int32_t chunk;     /* chunk length; must be 64                     */
+    int32_t chunk;     /* chunk length: 64 (16, 32 with KDA_FLAG_STAGED) */
     int32_t in_dtype;  /* kda_dtype of q, k, v, g, beta, dO            */
     int32_t out_dtype; /* kda_dtype of o, dq, dk, dv, dg, dbeta        */
     float l2_eps;      /* eps inside the L2 norm (1e-6 by default)     */
@@ -132,12 +133,15 @@ size_t kda_bwd_workspace_size(const kda_config* cfg, int64_t total_tokens, int32
  * pair formed directly, so any g <= 0; slow; meant as a cross-check of the
  * fused kernels, stage by stage.  o and final_state are as from kda_fwd.
  * KDA_FLAG_SAVE_FOR_BWD with it returns KDA_ERR_UNSUPPORTED; the other entry
- * points ignore the flag.
+ * points ignore the flag.  Under this flag alone cfg->chunk may also be 16 or
+ * 32 (C below), for chunk-size invariance checks: the chunking changes only
+ * rounding.
  *
- * Each stage is an fp32 array indexed [slot][head][...], where chunk j of
- * document n (tokens cu[n] + 64 j ..) has slot floor(cu[n] / 64) + n + j; a
- * chunk's rows (and Akk/Aqk/T columns) past its document's end are zero, and
- * slots no chunk maps to are left unwritten.  With G the in-chunk inclusive
+ * Each stage is an fp32 array indexed [slot][head][...], slots = total_tokens
+ * / C + num_seqs, where chunk j of document n (tokens cu[n] + C j ..) has slot
+ * floor(cu[n] / C) + n + j; a chunk's rows (and Akk/Aqk/T columns) past its
+ * document's end are zero, and slots no chunk maps to are left unwritten.
+ * Shapes below are for C = 64; for another C read C for 64.  With G the in-chunk inclusive
  * cumsum of g, qh, kh the normalised q (times scale) and k, E_rs =
  * exp(G_r - G_s) per channel: */
 typedef enum kda_stage {

@@ -11,5 +11,5 @@ hipError_t launch_decode(const DecodeParams&, int, int, int, hipStream_t) { retu
 hipError_t launch_segments(const SegParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_fwd_maps(const FwdParams&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_carry(const CarryParams&, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_fwd_staged(const StagedParams&, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_fwd_staged(const StagedParams&, int, int, int, int, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace kda

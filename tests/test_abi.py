@@ -218,6 +218,17 @@ def test_staged_forward_workspace_and_checks():
     need_s = _lib.kda_saved_size(both, T, N)
     assert _fwd(both, T=T, N=N, cu=FAKE, saved=FAKE, saved_bytes=need_s, ws=FAKE, wsb=need) == KDA_ERR_UNSUPPORTED
     assert "STAGED" in _err()
+    # chunks of 16 and 32: the staged forward only
+    c16 = _lib.make_config(H, dk, dv, KDA_BF16, KDA_F32, flags=_lib.KDA_FLAG_STAGED)
+    c16.chunk = 16
+    n16 = _lib.kda_fwd_workspace_size(c16, T, N)
+    assert n16 == _lib.kda_stage_offset(c16, T, N, len(_lib.STAGES)) > 0
+    assert _lib.kda_stage_offset(c16, T, N, 1) == (((T // 16 + N) * H * 16 * dk * 4) + 255) // 256 * 256
+    plain = _lib.make_config(H, dk, dv, KDA_BF16, KDA_F32)
+    plain.chunk = 16
+    assert _fwd(plain, T=T, N=N, cu=FAKE) == KDA_ERR_UNSUPPORTED and "chunk" in _err()
+    assert _lib.kda_bwd_raw(c16, T, N, *([FAKE] * 5), FAKE, 0, FAKE, 1 << 30, FAKE, 0, *([FAKE] * 5), 0,
+                            FAKE, 1 << 30, 0, "all") == KDA_ERR_UNSUPPORTED
 
 
 def test_head_count_bound():

@@ -38,7 +38,7 @@ def _stage_err(a, r):
     return float(np.abs(a - r).max()) / scale
 
 
-def _run(seed, lens, H, dk, dv, dtype, gates=None, out_dtype=None):
+def _run(seed, lens, H, dk, dv, dtype, gates=None, out_dtype=None, chunk=64):
     cu = kda_inputs.cu_from_lengths(lens)
     T = int(cu[-1])
     x = kda_inputs.generate(seed, T, H, dk, dv, dtype, num_seqs=len(lens), with_s0=True)
@@ -47,22 +47,24 @@ def _run(seed, lens, H, dk, dv, dtype, gates=None, out_dtype=None):
     t = {n: dev(x[n], dtype) for n in ("q", "k", "v", "g", "b")}
     s0 = torch.from_numpy(x["s0"]).cuda()
     cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
-    o, sf, st = kda.kda_fwd_staged(t["q"], t["k"], t["v"], t["g"], t["b"], cu_t, s0, out_dtype=out_dtype)
+    o, sf, st = kda.kda_fwd_staged(t["q"], t["k"], t["v"], t["g"], t["b"], cu_t, s0, out_dtype=out_dtype,
+                                   chunk=chunk)
     torch.cuda.synchronize()
     return cu, x, host(o), host(sf), {n: host(a) for n, a in st.items()}
 
 
-@pytest.mark.parametrize("dk,dv,dtype", [(64, 64, "bf16"), (128, 128, "bf16"), (64, 128, "f32"), (128, 64, "f32")])
-def test_stages_match_chunked_reference(dk, dv, dtype):
+@pytest.mark.parametrize("dk,dv,dtype,chunk", [(64, 64, "bf16", 64), (128, 128, "bf16", 64), (64, 128, "f32", 64),
+                                              (128, 64, "f32", 64), (128, 128, "bf16", 16), (64, 64, "f32", 32)])
+def test_stages_match_chunked_reference(dk, dv, dtype, chunk):
     need_gpu()
     H = 2
-    _say(f"stages dk={dk} dv={dv} {dtype} lens={LENS}")
-    cu, x, o, sf, st = _run(910 + dk + dv, LENS, H, dk, dv, dtype)
+    _say(f"stages dk={dk} dv={dv} {dtype} chunk={chunk} lens={LENS}")
+    cu, x, o, sf, st = _run(910 + dk + dv, LENS, H, dk, dv, dtype, chunk=chunk)
     ro, rsf, kept = chunked.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"],
-                                keep_stages=True)
+                                chunk=chunk, keep_stages=True)
     worst = {}
     for n, h, c0, ref in kept:
-        slot = int(cu[n]) // 64 + n + (c0 - int(cu[n])) // 64
+        slot = int(cu[n]) // chunk + n + (c0 - int(cu[n])) // chunk
         C = ref["Akk"].shape[0]
         got = {"G": st["G"][slot, h, :C], "Akk": st["Akk"][slot, h, :C, :C], "Aqk": st["Aqk"][slot, h, :C, :C],
                "T": st["T"][slot, h, :C, :C], "W": st["W"][slot, h, :C], "Ut": st["Ut"][slot, h, :C],
@@ -112,6 +114,23 @@ def test_staged_equal_sequences_and_bf16_output():
     cu = kda_inputs.cu_from_lengths([L] * N)
     ro, rsf = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu, initial_state=x["s0"])
     assert inf_rel(host(o32), ro) <= OUT_BAR and inf_rel(host(sf32), rsf) <= OUT_BAR
+
+
+def test_chunk_size_invariance():
+    """The chunking changes only rounding (the chunk form reaches the token
+    recurrence's result exactly): chunks of 16, 32 and 64 give o and the final
+    state within fp32 rounding of each other."""
+    need_gpu()
+    H, d = 2, 64
+    lens = [150, 64, 33]
+    res = {}
+    for chunk in (16, 32, 64):
+        _, _, o, sf, _ = _run(960, lens, H, d, d, "bf16", chunk=chunk)
+        res[chunk] = (o, sf)
+    for chunk in (16, 32):
+        eo, es = inf_rel(res[chunk][0], res[64][0]), inf_rel(res[chunk][1], res[64][1])
+        _say(f"chunk {chunk} against 64: o {eo:.1e}, final state {es:.1e}")
+        assert eo <= 1e-5 and es <= 1e-5
 
 
 def test_staged_against_fused_forward():
