@@ -919,15 +919,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const float FS = svmax * dsmax;                         // U/dU/S0/dS1/v products
     const float FO = qs > 0.f ? FS / qs : 0.f;              // products with dO
     // U rm (slot 4), dU rm (slot 7), dO rm (slot 6), v rm (slot 2), all fp16
+    // (each lane's VPH columns: DV/32 of them, 4 at dv = 128, 2 at dv = 64)
+    typedef float FV __attribute__((ext_vector_type(VPH)));
+    typedef _Float16 HV __attribute__((ext_vector_type(VPH)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ddr[i].keep(r0 + i < L);
         vvr[i].keep(r0 + i < L);
-        f32x4 dv4, vv4;
+        FV dvv, vvv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { dv4[e] = ddr[i][e] * ko; vv4[e] = vvr[i][e] * isv; }
-        *reinterpret_cast<f16::h4*>(Sx(6) + (r0 + i) * PV + cv0) = f16::cvt4(dv4);
-        *reinterpret_cast<f16::h4*>(Sx(2) + (r0 + i) * PV + cv0) = f16::cvt4(vv4);
+        for (int e = 0; e < VPH; ++e) { dvv[e] = ddr[i][e] * ko; vvv[e] = vvr[i][e] * isv; }
+        *reinterpret_cast<HV*>(Sx(6) + (r0 + i) * PV + cv0) = __builtin_convertvector(dvv, HV);
+        *reinterpret_cast<HV*>(Sx(2) + (r0 + i) * PV + cv0) = __builtin_convertvector(vvv, HV);
     }
     if (vact) {
         const float us = sscl[w], dus = sscl[DV / 16 + w];
