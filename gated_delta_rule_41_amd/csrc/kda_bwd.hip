@@ -967,6 +967,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             f32x4 a = zero;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                if (mb >= 2 && kk == 0) continue;   // T^T rows 32.. x columns ..31: zero (T is lower)
                 const V8T ah = lds_trT(S(0), PC, mb, kk, qg, cl);   // T^T
                 a = mma_k32(a, ah, bh[kk]);
                 a = mma_k32(a, ah, bl[kk]);
@@ -1115,7 +1116,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         for (int mb = 0; mb < 4; ++mb) {
             f32x4 x = zero;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) x = mma_k32(x, lds_trT(S(0), PC, mb, kk, qg, cl), th[kk]);
+            for (int kk = 0; kk < 2; ++kk)
+                if (!(mb >= 2 && kk == 0)) x = mma_k32(x, lds_trT(S(0), PC, mb, kk, qg, cl), th[kk]);   // T^T: upper
             put_blk<T, false>(Sh(0), Sh(0), PC, 16 * mb, nb, x, qg, cl, true);
         }
     }
@@ -1174,13 +1176,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = (nb + cl) * PC + 32 * kk + 8 * qg;
-                a = mma_k32(a, lds_trT(S(0), PC, mb, kk, qg, cl), whi[kk]);                  // T^T dW
-                const V8T kih = lds8<T>(S(2) + kb);
-                a = mma_k32(a, lds8<T>(Sh(0) + ka), kih);                                    // dAkk KI
-                qq = mma3<true>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + ka), kih, lds8<T>(S(6) + kb));   // dAqk KI
-                ki = mma_k32(ki, lds8<T>(QX + ka), lds8<T>(S(1) + kb));                      // dAkk^T KG
-                ki = mma3<true>(ki, lds8<T>(S(7) + ka), lds8<T>(Sh(7) + ka), lds8<T>(S(4) + kb),
-                                lds8<T>(S(5) + kb));                                         // dAqk^T QG
+                // blocks that the triangular factors make zero are skipped: T^T,
+                // dAkk^T, dAqk^T vanish for rows 32.. against columns ..31 (mb >= 2,
+                // kk = 0), dAkk and dAqk for rows ..31 against columns 32.. (mb <= 1,
+                // kk = 1)
+                if (!(mb >= 2 && kk == 0)) {
+                    a = mma_k32(a, lds_trT(S(0), PC, mb, kk, qg, cl), whi[kk]);              // T^T dW
+                    ki = mma_k32(ki, lds8<T>(QX + ka), lds8<T>(S(1) + kb));                  // dAkk^T KG
+                    ki = mma3<true>(ki, lds8<T>(S(7) + ka), lds8<T>(Sh(7) + ka), lds8<T>(S(4) + kb),
+                                    lds8<T>(S(5) + kb));                                     // dAqk^T QG
+                }
+                if (!(mb <= 1 && kk == 1)) {
+                    const V8T kih = lds8<T>(S(2) + kb);
+                    a = mma_k32(a, lds8<T>(Sh(0) + ka), kih);                                // dAkk KI
+                    qq = mma3<true>(qq, lds8<T>(S(3) + ka), lds8<T>(Sh(3) + ka), kih, lds8<T>(S(6) + kb));   // dAqk KI
+                }
             }
             dKG[mb] = a;
             dQG[mb] = qq;
