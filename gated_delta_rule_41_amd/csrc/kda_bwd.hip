@@ -636,6 +636,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     const _Float16* __restrict__ dS1 = reinterpret_cast<const _Float16*>(p.dst_saved) + (slot * H + h) * (int64_t)DK * DV;
     const float* __restrict__ s0sc = p.sv_scale + (slot * H + h) * (DV / 16);
     const float* __restrict__ d1sc = p.ds_scale + (slot * H + h) * (DV / 16);
+    // element (c, j) of the fp16 states: blocked by 16 value columns, [dv/16][dk][16]
+    auto blk16 = [](int c, int j) { return ((j >> 4) * DK + c) * 16 + (j & 15); };
     // S0 / dS1 row fragments (loaded during Akk and T), kept in fp16 until used
     typedef _Float16 h8v __attribute__((ext_vector_type(8)));
     typedef _Float16 h4v __attribute__((ext_vector_type(4)));
@@ -820,7 +822,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     if (kact) {
         const int nr = 16 * w + cl;
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) xs0[kk] = *reinterpret_cast<const h8v*>(S0 + (nr * DV + 32 * kk + 8 * qg));
+        for (int kk = 0; kk < NKV; ++kk) xs0[kk] = *reinterpret_cast<const h8v*>(S0 + blk16(nr, 32 * kk + 8 * qg));
     }
     // ================= Akk (fp32 -> slot 5) =================
     float* const Af = Sf(5);
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     if (kact) {
         const int nr = 16 * w + cl;
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) xd0[kk] = *reinterpret_cast<const h8v*>(dS1 + (nr * DV + 32 * kk + 8 * qg));
+        for (int kk = 0; kk < NKV; ++kk) xd0[kk] = *reinterpret_cast<const h8v*>(dS1 + blk16(nr, 32 * kk + 8 * qg));
     }
     // off-diagonal blocks, column j on wave j: T_ij = -T_ii sum_{k=j}^{i-1} Akk_ik T_kj
     {

@@ -182,7 +182,9 @@ __device__ void exact_chunk(const BwdParams& p, ExactLds<DK>& sm, int64_t slot, 
     auto ld4 = [&](const void* base, const float* scale, int c, int j) -> f32x4 {
         if constexpr (std::is_same<T, bf16>::value) {
             typedef _Float16 h4v __attribute__((ext_vector_type(4)));
-            const h4v x = *reinterpret_cast<const h4v*>(reinterpret_cast<const _Float16*>(base) + sbase + (int64_t)c * DV + j);
+            // fp16 states are blocked by 16 value columns: [dv/16][dk][16]
+            const h4v x = *reinterpret_cast<const h4v*>(reinterpret_cast<const _Float16*>(base) + sbase +
+                                                        (int64_t)((j >> 4) * DK + c) * 16 + (j & 15));
             return __builtin_convertvector(x, f32x4) * scale[(slot * H + h) * (DV / 16) + (j >> 4)];
         } else {
             (void)scale;

@@ -267,15 +267,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 }
                 if (SAVE) {
                     // entering state of this chunk: the scaled state in fp16 (|S| < 2^6
-                    // here) and 2^e of this wave's 16 columns
-                    // (each 16x16 block turned into rows of four by the matrix core,
-                    // so that a lane stores 8 bytes at a time)
-                    h16* st = reinterpret_cast<h16*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv;
-                    const unsigned lane_off = (unsigned)(cl * dv + dv0 + 16 * w + 4 * qg);
+                    // here) and 2^e of this wave's 16 columns.  Saved blocked by 16
+                    // value columns ([dv/16][dk][16]), so this wave's dk x 16 block is
+                    // contiguous; each 16x16 block is turned into rows of four by the
+                    // matrix core, so that one store writes 512 contiguous bytes
+                    h16* st = reinterpret_cast<h16*>(p.st_saved) + (slot * H + h) * (int64_t)DK * dv +
+                              ((dv0 >> 4) + w) * DK * 16;
+                    const unsigned lane_off = (unsigned)(cl * 16 + 4 * qg);
                     const h4 eye4 = block_eye4(qg, cl);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
-                        *reinterpret_cast<h4*>(at32(st + 16 * mb * dv, lane_off)) = block_rows4(S[mb], eye4);
+                        *reinterpret_cast<h4*>(at32(st + 256 * mb, lane_off)) = block_rows4(S[mb], eye4);
                     if (l == 0) p.sv_scale[(slot * H + h) * (dv / 16) + (dv0 >> 4) + w] = usc;
                 }
                 if (safe) {

@@ -201,13 +201,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                 }
                 {
                     // dL/dS at the end of this chunk: the scaled values in fp16 and
-                    // 2^e of this wave's 16 columns
-                    h16* out = dst + (slot * H + h) * (int64_t)DK * dv;
-                    const unsigned lane_off = (unsigned)(qg * 4 * dv + vcol);
+                    // 2^e of this wave's 16 columns, blocked by 16 value columns
+                    // ([dv/16][dk][16]) as the forward saves its states
+                    h16* out = dst + (slot * H + h) * (int64_t)DK * dv + ((dv0 >> 4) + w) * DK * 16;
+                    const unsigned lane_off = (unsigned)(qg * 64 + cl);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) *at32(out + (16 * mb + i) * dv, lane_off) = (h16)dS[mb][i];
+                        for (int i = 0; i < 4; ++i) *at32(out + (16 * mb + i) * 16, lane_off) = (h16)dS[mb][i];
                     if (l == 0) p.ds_scale[(slot * H + h) * (dv / 16) + (dv0 >> 4) + w] = usc;
                 }
                 if (safe) {
