@@ -622,8 +622,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // per-lane offsets inside a chunk fit in 32 bits (64 H max(dk, dv) < 2^31 is
     // checked on the host); only the chunk bases are 64-bit
     const int rk32 = (int)rsk, rv32 = (int)rsv;
-    const float* __restrict__ nqc = p.nq_saved + c0 * H + h;
-    const float* __restrict__ nkc = p.nk_saved + c0 * H + h;
+    const float* __restrict__ nqc = p.nq_saved + (int64_t)h * p.T + c0;   // norms: head-major [H, T]
+    const float* __restrict__ nkc = p.nk_saved + (int64_t)h * p.T + c0;
     const T* __restrict__ qc = reinterpret_cast<const T*>(p.q) + c0 * rsk + h * DK;
     const T* __restrict__ kc = reinterpret_cast<const T*>(p.k) + c0 * rsk + h * DK;
     const T* __restrict__ gcp = reinterpret_cast<const T*>(p.g) + c0 * rsk + h * DK;
@@ -672,8 +672,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             R.k[i].load(kc + (rc * rk32 + ck0));
             R.g[i].load(gcp + (rc * rk32 + ck0));
             R.rb[i] = gload1(bc + rc * H);
-            R.nq[i] = nqc[rc * H];     // norms saved by the forward
-            R.nk[i] = nkc[rc * H];
+            R.nq[i] = nqc[rc];     // norms saved by the forward
+            R.nk[i] = nkc[rc];
         }
     };
     auto prep_finish = [&](Prep& P, PrepRaw& R, bool first) {
@@ -1470,8 +1470,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_chunk_f32_kernel(BwdParam
                 gload<T, VPL>(vv[i], vp + (tok * H + h) * DV + VPL * cl);
                 gload<T, VPL>(dov[i], dop + (tok * H + h) * DV + VPL * cl);
                 rb[i] = gload1(bp + tok * H + h);
-                nq[i] = p.nq_saved[tok * H + h];     // norms saved by the forward
-                nk[i] = p.nk_saved[tok * H + h];
+                nq[i] = p.nq_saved[(int64_t)h * p.T + tok];     // norms saved by the forward ([H, T])
+                nk[i] = p.nk_saved[(int64_t)h * p.T + tok];
             } else {
 #pragma unroll
                 for (int e = 0; e < CPL; ++e) { qh[i][e] = 0.f; kh[i][e] = 0.f; rg[i][e] = 0.f; }

@@ -66,8 +66,8 @@ __global__ __launch_bounds__(kThreads) void kda_fwd_token_kernel(FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) st[(int64_t)(16 * mb + 4 * qg + i) * dv + col] = S[mb][i];
         }
-        token_fwd<T, TO, DK>(S, src, c0, L, op, SAVE ? p.nq_saved : nullptr, SAVE ? p.nk_saved : nullptr,
-                             slice == 0 && tid == 0);
+        token_fwd<T, TO, DK>(S, src, c0, L, op, SAVE ? p.nq_saved + (int64_t)h * p.T : nullptr,
+                             SAVE ? p.nk_saved + (int64_t)h * p.T : nullptr, slice == 0 && tid == 0);
     }
     if (p.sfinal) {
 #pragma unroll

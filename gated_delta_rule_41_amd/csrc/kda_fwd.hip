@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_fwd_kernel(FwdParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * w + 4 * qg + i;
                 if (r < L) {
-                    p.nq_saved[(c0 + r) * H + h] = nq[i];
-                    p.nk_saved[(c0 + r) * H + h] = nk[i];
+                    p.nq_saved[(int64_t)h * p.T + c0 + r] = nq[i];   // head-major [H, T]
+                    p.nk_saved[(int64_t)h * p.T + c0 + r] = nk[i];
                 }
             }
         }

@@ -599,8 +599,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 // state wave pw forms in phase B (it has the time there)
                 sm.ninv[pw][l] = __builtin_shufflevector(cvt4(d1), cvt4(d2), 0, 1, 2, 3, 4, 5, 6, 7);
                 if (SAVE && slice == 0 && qg == 0 && rr < Lm) {
-                    p.nq_saved[(cm + rr) * H + h] = sqrtf(ssq);
-                    p.nk_saved[(cm + rr) * H + h] = sqrtf(ssk);
+                    // head-major [H, T]: the block's 16 rows are 64 contiguous bytes
+                    p.nq_saved[(int64_t)h * p.T + cm + rr] = sqrtf(ssq);
+                    p.nk_saved[(int64_t)h * p.T + cm + rr] = sqrtf(ssk);
                 }
             }
             lds_barrier();

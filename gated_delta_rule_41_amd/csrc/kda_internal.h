@@ -65,8 +65,8 @@ struct FwdParams {
     // inputs: states and U in fp16, scaled by 2^-e per (slot, head, 16-column
     // group), with 2^e in sv_scale.
     void* st_saved;      // [slots,H,dk,dv]: the state entering every chunk
-    float* nq_saved;     // [T,H] or nullptr
-    float* nk_saved;     // [T,H] or nullptr
+    float* nq_saved;     // [H,T] (head-major) or nullptr
+    float* nk_saved;     // [H,T] (head-major) or nullptr
     void* u_saved;       // [slots,H,dv,64] fp16 (column-major per chunk): U of every chunk (bf16 inputs)
     float* sv_scale;     // [slots,H,dv/16] fp32: 2^e of the saved state and U (bf16 inputs)
     const int32_t* sf_dst;   // per sequence: row of sfinal to write, or -1 to skip; nullptr = itself

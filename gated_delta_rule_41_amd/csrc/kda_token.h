@@ -118,8 +118,8 @@ __device__ void token_fwd(f32x4 (&S)[DK / 16], const TokSrc<T>& src, int64_t c0,
         const float o = qg_sum(oo) * (src.scale / nq);
         if (op && src.qg == 0) op[(tok * src.H + src.h) * (int64_t)src.dv + src.col] = from_f32<TO>(o);
         if (nq_out && wnorm) {
-            nq_out[tok * src.H + src.h] = nq;
-            nk_out[tok * src.H + src.h] = nk;
+            nq_out[tok] = nq;   // this head's row of the head-major norms
+            nk_out[tok] = nk;
         }
         cur = nxt;
     }
