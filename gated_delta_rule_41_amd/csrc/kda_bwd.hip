@@ -800,8 +800,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             const _Float16* __restrict__ ub = reinterpret_cast<const _Float16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * DV;
             const _Float16* __restrict__ dub = reinterpret_cast<const _Float16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * DV;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {   // column-major [dv][64]: four rows per 8-byte load
-                const int o = (16 * wv + cl) * kChunk + 16 * mb + 4 * qg;
+            for (int mb = 0; mb < 4; ++mb) {   // fragment order (ufrag): 512 contiguous bytes per load
+                const int o = ((4 * wv + mb) * 64 + l) * 4;
                 Uh[mb] = *reinterpret_cast<const h4v*>(ub + o);
                 dUh[mb] = *reinterpret_cast<const h4v*>(dub + o);
             }

@@ -58,6 +58,14 @@ __device__ __forceinline__ float qsum(float v) {
     return v + __shfl_xor(v, 32);
 }
 
+// U and dU of a chunk (fp16, per head [64 tokens][dv]) are stored in MFMA
+// fragment order: 16-column group g = j >> 4, then row block ib = t >> 4, then
+// the accumulator lane (qg = (t >> 2) & 3, cl = j & 15), then i = t & 3, so that
+// the 16x16 block a wave holds in an accumulator is 512 contiguous bytes.
+__host__ __device__ constexpr int ufrag(int t, int j) {
+    return (((j >> 4) * 4 + (t >> 4)) * 64 + ((t >> 2) & 3) * 16 + (j & 15)) * 4 + (t & 3);
+}
+
 constexpr float kUnsafe = -14.f;   // lowest per-block log2 decay the fp16 factors hold
 
 

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                         const float o = MAP ? 0.f : qsum(oo) * (p.scale / sqrtf(qsum(sqq) + p.eps)) * usc;
                         if (qg == 0) {
                             if (!MAP) op[(tok * H + h) * dv + vcol] = from_f32<TO>(o);
-                            if (SAVE) reinterpret_cast<h16*>(p.u_saved)[((slot * H + h) * dv + vcol) * kChunk + t] = (h16)u;
+                            if (SAVE) reinterpret_cast<h16*>(p.u_saved)[(slot * H + h) * (int64_t)kChunk * dv + ufrag(t, vcol)] = (h16)u;
                         }
                     }
                 }
@@ -381,10 +381,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_fwd16_kernel(FwdParams p)
                 uf[0] = __builtin_shufflevector(ub[0], ub[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 uf[1] = __builtin_shufflevector(ub[2], ub[3], 0, 1, 2, 3, 4, 5, 6, 7);
                 if (SAVE) {
-                    // U of this chunk in fp16, scaled like the saved state
-                    h16* ubase = reinterpret_cast<h16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * dv;
+                    // U of this chunk in fp16, scaled like the saved state, in MFMA
+                    // fragment order (ufrag): each store is 512 contiguous bytes
+                    h16* ubase = reinterpret_cast<h16*>(p.u_saved) + (slot * H + h) * (int64_t)kChunk * dv +
+                                 ((dv0 >> 4) + w) * 1024;
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<h4*>(at32(ubase, vcol * kChunk + 16 * ib + 4 * qg)) = ub[ib];
+                    for (int ib = 0; ib < 4; ++ib) *reinterpret_cast<h4*>(at32(ubase, 256 * ib + 4 * l)) = ub[ib];
                 }
                 pend = true;
             }

@@ -67,7 +67,7 @@ struct FwdParams {
     void* st_saved;      // [slots,H,dk,dv]: the state entering every chunk
     float* nq_saved;     // [H,T] (head-major) or nullptr
     float* nk_saved;     // [H,T] (head-major) or nullptr
-    void* u_saved;       // [slots,H,dv,64] fp16 (column-major per chunk): U of every chunk (bf16 inputs)
+    void* u_saved;       // [slots,H,64*dv] fp16 in fragment order (ufrag): U of every chunk (bf16 inputs)
     float* sv_scale;     // [slots,H,dv/16] fp32: 2^e of the saved state and U (bf16 inputs)
     const int32_t* sf_dst;   // per sequence: row of sfinal to write, or -1 to skip; nullptr = itself
     int64_t T;
@@ -128,8 +128,8 @@ struct BwdParams {
     const float* dS_final;   // [N,H,dk,dv] or nullptr
     void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
                              // (fp32 for fp32 inputs; fp16 scaled by ds_scale for bf16 inputs)
-    const void* u_saved;     // forward's U of every chunk [slots,H,dv,64] fp16 (bf16 inputs)
-    void* du_ws;             // workspace: dU of every chunk [slots,H,dv,64] fp16 (bf16 inputs)
+    const void* u_saved;     // forward's U of every chunk [slots,H,64*dv] fp16, fragment order (bf16 inputs)
+    void* du_ws;             // workspace: dU of every chunk, the same layout (bf16 inputs)
     const float* sv_scale;   // [slots,H,dv/16]: 2^e of the saved state and U (bf16 inputs)
     float* ds_scale;         // workspace [slots,H,dv/16]: 2^e of dS1 and dU (bf16 inputs)
     int32_t* chunk_flags;    // workspace [slots,H]: 1 where the chunk's decay passes the factorised

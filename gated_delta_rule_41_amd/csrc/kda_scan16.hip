@@ -268,10 +268,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                 }
                 yf[0] = __builtin_shufflevector(yb[0], yb[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 yf[1] = __builtin_shufflevector(yb[2], yb[3], 0, 1, 2, 3, 4, 5, 6, 7);
-                // dU of this chunk in fp16 (scaled like dS1), column-major [dv][64]
-                h16* ub = reinterpret_cast<h16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * dv;
+                // dU of this chunk in fp16 (scaled like dS1), in MFMA fragment order
+                // as the forward's U (ufrag): each store is 512 contiguous bytes
+                h16* ub = reinterpret_cast<h16*>(p.du_ws) + (slot * H + h) * (int64_t)kChunk * dv + ((dv0 >> 4) + w) * 1024;
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb) *reinterpret_cast<h4*>(at32(ub, vcol * kChunk + 16 * sb + 4 * qg)) = cvt4(dU[sb]);
+                for (int sb = 0; sb < 4; ++sb) *reinterpret_cast<h4*>(at32(ub, 256 * sb + 4 * l)) = cvt4(dU[sb]);
                 pend = true;
             }
             lds_barrier();
