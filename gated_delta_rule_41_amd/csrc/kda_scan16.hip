@@ -203,12 +203,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_scan16_kernel(BwdPara
                     // dL/dS at the end of this chunk: the scaled values in fp16 and
                     // 2^e of this wave's 16 columns, blocked by 16 value columns
                     // ([dv/16][dk][16]) as the forward saves its states
+                    // (each 16x16 block turned into rows of four by the matrix core:
+                    // one store writes 512 contiguous bytes)
                     h16* out = dst + (slot * H + h) * (int64_t)DK * dv + ((dv0 >> 4) + w) * DK * 16;
-                    const unsigned lane_off = (unsigned)(qg * 64 + cl);
+                    const unsigned lane_off = (unsigned)(cl * 16 + 4 * qg);
+                    const h4 eye4 = block_eye4(qg, cl);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) *at32(out + (16 * mb + i) * 16, lane_off) = (h16)dS[mb][i];
+                        *reinterpret_cast<h4*>(at32(out + 256 * mb, lane_off)) = block_rows4(dS[mb], eye4);
                     if (l == 0) p.ds_scale[(slot * H + h) * (dv / 16) + (dv0 >> 4) + w] = usc;
                 }
                 if (safe) {
