@@ -33,9 +33,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Saved per-chunk states and state gradients: fp32 for fp32 inputs; fp16 with
-// a power-of-two scale per 16-column group for bf16 inputs (the fp16 kernels
-// hold them as fp16-safe scaled values already).
+// Saved per-chunk states and state gradients: fp32 [dk][dv] for fp32 inputs;
+// fp16 with a power-of-two scale per 16-column group for bf16 inputs (the fp16
+// kernels hold them as fp16-safe scaled values already), blocked by those 16
+// columns ([dv/16][dk][16]) so that each wave's save is contiguous.
 size_t state_elem_bytes(const kda_config* c) { return c->in_dtype == KDA_BF16 ? 2 : 4; }
 
 // The scales of the fp16 saves: one fp32 per (slot, head, 16-column group).
@@ -99,8 +100,9 @@ kda_status opt_ptr(const void* p, const char* name) {
     return KDA_OK;
 }
 
-// Per-chunk U (forward) and dU (reverse scan), fp16 [slots, H, dv, 64] (bf16
-// inputs): the bf16 chunk-gradient kernel reads them instead of recomputing both.
+// Per-chunk U (forward) and dU (reverse scan), fp16, 64 x dv per (slot, head) in
+// MFMA fragment order (ufrag in kda_f16.h) (bf16 inputs): the bf16 chunk-gradient
+// kernel reads them instead of recomputing both.
 size_t chunk_u_bytes(const kda_config* c, int64_t T, int32_t N) {
     if (c->in_dtype != KDA_BF16) return 0;
     return (size_t)kda::num_slots(T, N) * c->H * kda::kChunk * c->dv * 2;

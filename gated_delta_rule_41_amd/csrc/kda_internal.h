@@ -64,7 +64,8 @@ struct FwdParams {
     // Saves for the backward (or nullptr).  fp32 inputs: states fp32.  bf16
     // inputs: states and U in fp16, scaled by 2^-e per (slot, head, 16-column
     // group), with 2^e in sv_scale.
-    void* st_saved;      // [slots,H,dk,dv]: the state entering every chunk
+    void* st_saved;      // the state entering every chunk: fp32 [slots,H,dk,dv], or (bf16
+                         // inputs) fp16 blocked by 16 value columns [slots,H,dv/16,dk,16]
     float* nq_saved;     // [H,T] (head-major) or nullptr
     float* nk_saved;     // [H,T] (head-major) or nullptr
     void* u_saved;       // [slots,H,64*dv] fp16 in fragment order (ufrag): U of every chunk (bf16 inputs)
@@ -126,7 +127,7 @@ struct BwdParams {
     const float* nk_saved;
     const void* dO;          // [T,H,dv] in dtype
     const float* dS_final;   // [N,H,dk,dv] or nullptr
-    void* dst_saved;         // workspace: dL/dS at the END of every chunk [slots,H,dk,dv]
+    void* dst_saved;         // workspace: dL/dS at the END of every chunk (layout of st_saved)
                              // (fp32 for fp32 inputs; fp16 scaled by ds_scale for bf16 inputs)
     const void* u_saved;     // forward's U of every chunk [slots,H,64*dv] fp16, fragment order (bf16 inputs)
     void* du_ws;             // workspace: dU of every chunk, the same layout (bf16 inputs)
