@@ -757,11 +757,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             }
         }
     };
+    // The transposed [c][s] tiles (KG^T, KI^T, QG^T) swizzle their 8-element
+    // groups by row: group g of row c sits at g ^ ((c >> 2) & 7).  A lane of
+    // put_tp writes row ck0 + e, and rows four apart would otherwise fall on
+    // the same banks.
+    auto tsw = [](int c, int g) { return c * PC + 8 * (g ^ ((c >> 2) & 7)); };
     auto put_tp = [&](const Prep& P, T* hi, T* lo, auto val, bool split) {
 #pragma unroll
         for (int e = 0; e < CPH; ++e) {
             const f32x4 x = {val(P, 0, e), val(P, 1, e), val(P, 2, e), val(P, 3, e)};
-            const int o = (ck0 + e) * PC + r0;
+            const int o = tsw(ck0 + e, r0 >> 3) + (r0 & 7);
             if (split) sts4_split<T, true>(hi + o, lo + o, x);
             else sts4<T>(hi + o, x);
         }
@@ -1177,7 +1182,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
             f32x4 a = zero, qq = dQG[mb], ki = zero;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = (nb + cl) * PC + 32 * kk + 8 * qg;
+                const int ka = (16 * mb + cl) * PC + 32 * kk + 8 * qg, kb = tsw(nb + cl, 4 * kk + qg);
                 // blocks that the triangular factors make zero are skipped: T^T,
                 // dAkk^T, dAqk^T vanish for rows 32.. against columns ..31 (mb >= 2,
                 // kk = 0), dAkk and dAqk for rows ..31 against columns 32.. (mb <= 1,
