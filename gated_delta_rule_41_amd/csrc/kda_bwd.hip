@@ -1210,33 +1210,48 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     // (the chain rule's rows go out now and arrive during the transposes)
     PrepRaw R3;
     prep_load(R3);
-    constexpr int LDF = DK + 4;
     float* const F0 = Sf(0);   // slots 0-1
     float* const F1 = Sf(2);   // slots 2-3
     float* const F2 = Sf(4);   // slots 4-5
     float* const F3 = Sf(6);   // slots 6-7
-    static_assert(kChunk * LDF * 4 <= 2 * LY::SLOT, "fp32 staging");
+    static_assert(DK * kChunk * 4 <= 2 * LY::SLOT, "fp32 staging");
+    // The staging tiles are transposed, [key column c][row r], 64 floats per
+    // column: an accumulator block (rows 16mb + 4qg + i, column 16w + cl) goes
+    // in as one 16-byte store per lane and the prep layout (rows r0..r0+3,
+    // column ck0 + e) comes out as one 16-byte load.  The 4-row group g of
+    // column c sits at g ^ f(c), f's bits being c0^c2, c0^c3, c1^c4, c0^c5, which
+    // keeps both the stores (8 lanes on consecutive columns) and the loads (16
+    // lanes on columns four apart) free of bank conflicts.
+    auto fst = [](int c, int g) {
+        const int f = ((c ^ (c >> 2)) & 1) | (((c ^ (c >> 3)) & 1) << 1) | ((((c >> 1) ^ (c >> 4)) & 1) << 2) |
+                      (((c ^ (c >> 5)) & 1) << 3);
+        return c * kChunk + 4 * (g ^ f);
+    };
     float gQ[4][CPH], gKG[4][CPH], gKI[4][CPH], gKt[4][CPH];
     if (kact) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            st_blk(F0, LDF, 16 * mb, 16 * w, dQG[mb], qg, cl);
-            st_blk(F1, LDF, 16 * mb, 16 * w, dKG[mb], qg, cl);
-            st_blk(F2, LDF, 16 * mb, 16 * w, dKI[mb], qg, cl);
-            st_blk(F3, LDF, 16 * mb, 16 * w, dKt[mb], qg, cl);
+            const int o = fst(16 * w + cl, 4 * mb + qg);
+            *reinterpret_cast<f32x4*>(F0 + o) = dQG[mb];
+            *reinterpret_cast<f32x4*>(F1 + o) = dKG[mb];
+            *reinterpret_cast<f32x4*>(F2 + o) = dKI[mb];
+            *reinterpret_cast<f32x4*>(F3 + o) = dKt[mb];
         }
     }
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < CPH; ++e) {
+        const int o = fst(ck0 + e, r0 >> 2);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(F0 + o), b = *reinterpret_cast<const f32x4*>(F1 + o),
+                    c = *reinterpret_cast<const f32x4*>(F2 + o), d = *reinterpret_cast<const f32x4*>(F3 + o);
 #pragma unroll
-        for (int e = 0; e < CPH; ++e) {
-            const int o = (r0 + i) * LDF + ck0 + e;
-            gQ[i][e] = F0[o];
-            gKG[i][e] = F1[o];
-            gKI[i][e] = F2[o];
-            gKt[i][e] = F3[o];
+        for (int i = 0; i < 4; ++i) {
+            gQ[i][e] = a[i];
+            gKG[i][e] = b[i];
+            gKI[i][e] = c[i];
+            gKt[i][e] = d[i];
         }
+    }
 
     // ================= chain rule to qh, kh, beta, G =================
     Prep P;
