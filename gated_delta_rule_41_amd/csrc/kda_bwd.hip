@@ -851,9 +851,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
     lds_barrier();
     // ================= T = (I + Akk)^{-1} (fp32 in slot 7) =================
     float* const Tf = Sf(7);
-    for (int e = tid; e < kChunk * PF; e += kWideThreads) {
-        const int r = e / PF, c = e % PF;
-        if ((r >> 4) != (c >> 4) || c >= kChunk) Tf[e] = 0.f;
+    // the six 16 x 16 blocks above the diagonal are zero; waves 4-7 clear them
+    // (384 16-byte pieces) while waves 0-3 invert the diagonal blocks, and the
+    // blocks below are written by the solve (columns past 64 are never read)
+    if (w >= 4) {
+        for (int e = tid - 256; e < 384; e += 256) {
+            const int pr = e >> 6, row = (e >> 2) & 15, q4 = e & 3;
+            const int bi = pr < 3 ? 0 : (pr < 5 ? 1 : 2), bj = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+            *reinterpret_cast<f32x4*>(&Tf[(16 * bi + row) * PF + 16 * bj + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     if (w < 4) {
         const f32x4 na = *reinterpret_cast<const f32x4*>(&Af[(16 * w + cl) * PF + 16 * w + 4 * qg]);
