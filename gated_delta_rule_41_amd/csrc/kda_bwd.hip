@@ -1135,12 +1135,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
         }
     }
     lds_barrier();
-    // ================= dAkk = -strict(X T^T) (waves 0-3) =================
-    f32x4 dAkk[4];
-    if (w < 4) {
-        const int nb = 16 * w;
+    // ================= dAkk = -strict(X T^T) (all waves) =================
+    // column block nb on waves w and w + 4: row blocks 0-1 on waves 0-3, 2-3 on
+    // waves 4-7 (an even split measured faster; the same split of Akk did not)
+    f32x4 dAkk[2];
+    {
+        const int nb = 16 * wl;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int m = 0; m < 2; ++m) {
+            const int mb = 2 * wh + m;
             // a: dAkk[16mb+4qg+i][nb+cl]; at: operands swapped, dAkk[16mb+cl][nb+4qg+i]
             f32x4 a = zero, at = zero;
 #pragma unroll
@@ -1156,18 +1159,20 @@ __global__ __launch_bounds__(kWideThreads, 1) void kda_bwd_grads_kernel(BwdParam
                 at[i] = nb + 4 * qg + i < 16 * mb + cl ? -at[i] : 0.f;
             }
             sts4<T>(QX + (nb + cl) * PC + 16 * mb + 4 * qg, a);   // dAkk^T [s][r]
-            dAkk[mb] = at;
+            dAkk[m] = at;
         }
     }
     lds_barrier();
     // tiles for the last products:
     //   dAkk rm [r][s] (slot 0, 2nd half), dAkk^T [s][r] (QX), dAqk rm h/l (slot 3),
     //   dAqk^T h/l (slot 7), KI^T h/l [c][s] (slots 2, 6), QG^T h/l [c][r] (slots 4, 5)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        sts4<T>(Sh(0) + (16 * (2 * wh + m) + cl) * PC + 16 * wl + 4 * qg, dAkk[m]);   // dAkk rm [r][s]
     if (w < 4) {
         const int nb = 16 * w;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            sts4<T>(Sh(0) + (16 * mb + cl) * PC + nb + 4 * qg, dAkk[mb]);   // dAkk rm [r][s]
             const int o = (nb + cl) * PC + 16 * mb + 4 * qg;                // dAqk^T h/l [s][r]
             sts4_split<T, SPLIT>(S(7) + o, Sh(7) + o, dAqk[mb]);
         }
